@@ -1,0 +1,184 @@
+"""Oracle: the data-moving and arithmetic stages of the layer (test infrastructure).
+
+Plain numpy, float64 arithmetic on whatever values the caller passes (the
+tests pass bf16-rounded inputs converted to float64).
+
+The method only relocates work: a slot row is a bitwise copy of a home row
+and a direct read of a home row gives the same numbers ([P2] "Core technique"
+and "Memory contract and weight layout"), so every float result here also has
+a plan-independent definition (``moe_forward``, ``expert_weight_grad``) that
+the tests hold the planned chain to.
+
+Layout contract ([P2] "Memory contract and weight layout"):
+  * Xp, Yp, dY: [R*S*K, D] rows; rank r owns rows [r*P, (r+1)*P), P = S*K;
+    inside a rank, group g owns rows [cu[r,g], cu[r,g+1]).
+  * Rank r's weight row g is W_home[g] for g < E and W_slots[r, g-E] for
+    g >= E.
+  * Gradients are float32 buffers of the same shapes; rows [E, E+B) of each
+    rank are its reduce buffers, viewed together as [R, B, H, H'].
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def dispatch(X: np.ndarray, dest_idx: np.ndarray) -> np.ndarray:
+    """Fused permute: row dest_idx[r,s,k] of the output is token (r, s) of X ([P2] "Core technique")."""
+    R, S, H = X.shape
+    K = dest_idx.shape[2]
+    Xp = np.empty((R * S * K, H), dtype=X.dtype)
+    Xp[np.asarray(dest_idx).reshape(-1)] = np.repeat(X.reshape(R * S, H), K, axis=0)
+    return Xp
+
+
+def prefetch(W_home: np.ndarray, slot_expert: np.ndarray, W_slots: np.ndarray | None = None) -> np.ndarray:
+    """Slot j of rank r receives a copy of home expert slot_expert[r, j]; -1 leaves it as is."""
+    R, B = slot_expert.shape
+    E, H, Hp = W_home.shape
+    out = np.zeros((R, B, H, Hp), dtype=W_home.dtype) if W_slots is None else W_slots.copy()
+    for r in range(R):
+        for j in range(B):
+            if slot_expert[r, j] >= 0:
+                out[r, j] = W_home[slot_expert[r, j]]
+    return out
+
+
+def rank_weight(W_home, W_slots, r: int, g: int):
+    """Weight row g of rank r's logical [E+B, H, H'] tensor."""
+    E = W_home.shape[0]
+    return W_home[g] if g < E else W_slots[r, g - E]
+
+
+def row_group(cu_seqlens: np.ndarray, P: int, rows: np.ndarray):
+    """(rank, group) of each dispatched row."""
+    rows = np.asarray(rows, dtype=np.int64)
+    ranks = rows // P
+    local = rows % P
+    groups = np.array([np.searchsorted(cu_seqlens[r], l, side="right") - 1 for r, l in zip(ranks, local)],
+                      dtype=np.int64)
+    return ranks, groups
+
+
+def group_gemm(Xp, W_home, W_slots, cu_seqlens, P: int, rows=None) -> np.ndarray:
+    """Yp[rows of group g on rank r] = Xp[those rows] @ W_r[g] ([P2] "Memory contract": VM group GEMM).
+
+    With ``rows`` given, returns only those output rows (Xp must then be the full
+    buffer or any array indexable by the row ids).
+    """
+    R = cu_seqlens.shape[0]
+    G = cu_seqlens.shape[1] - 1
+    Hp = W_home.shape[2]
+    if rows is None:
+        Y = np.zeros((Xp.shape[0], Hp), dtype=np.float64)
+        for r in range(R):
+            for g in range(G):
+                a, b = r * P + cu_seqlens[r, g], r * P + cu_seqlens[r, g + 1]
+                if b > a:
+                    Y[a:b] = Xp[a:b].astype(np.float64) @ rank_weight(W_home, W_slots, r, g).astype(np.float64)
+        return Y
+    ranks, groups = row_group(cu_seqlens, P, rows)
+    Y = np.zeros((len(rows), Hp), dtype=np.float64)
+    for i, (row, r, g) in enumerate(zip(rows, ranks, groups)):
+        Y[i] = Xp[row].astype(np.float64) @ rank_weight(W_home, W_slots, r, g).astype(np.float64)
+    return Y
+
+
+def combine(Yp: np.ndarray, dest_idx: np.ndarray, gates: np.ndarray, tokens=None) -> np.ndarray:
+    """Fused unpermute: out[r,s] = sum_k gate[r,s,k] * Yp[dest_idx[r,s,k]] ([P2] "Core technique").
+
+    ``tokens`` (flat r*S+s ids) restricts the result to those tokens.
+    """
+    R, S, K = dest_idx.shape
+    D = Yp.shape[1]
+    dflat = np.asarray(dest_idx).reshape(R * S, K)
+    gflat = np.asarray(gates, dtype=np.float64).reshape(R * S, K)
+    tok = np.arange(R * S) if tokens is None else np.asarray(tokens)
+    out = np.zeros((len(tok), D), dtype=np.float64)
+    for k in range(K):
+        out += gflat[tok, k:k + 1] * Yp[dflat[tok, k]].astype(np.float64)
+    return out if tokens is not None else out.reshape(R, S, D)
+
+
+def combine_abs(Yp, dest_idx, gates, tokens=None) -> np.ndarray:
+    """sum_k |gate * y|: the scale of the combine sum, used for its error bound."""
+    return combine(np.abs(np.asarray(Yp, dtype=np.float64)), dest_idx, np.abs(gates), tokens)
+
+
+def wgrad(Xp, dY, cu_seqlens, P: int, dW_home, dW_slots, dtype=np.float64):
+    """dW_r[g] += Xp[rows_g]^T @ dY[rows_g] for every rank and group ([P2] "Memory contract").
+
+    Groups g < E add into dW_home[g] (ranks in ascending order: the home rank's
+    kept rows and other ranks' direct reads of that home row); slot groups add
+    into that rank's reduce buffer dW_slots[r, g-E].  Works in place.
+    """
+    R = cu_seqlens.shape[0]
+    E = dW_home.shape[0]
+    G = cu_seqlens.shape[1] - 1
+    for g in range(G):
+        for r in range(R):
+            a, b = r * P + cu_seqlens[r, g], r * P + cu_seqlens[r, g + 1]
+            if b <= a:
+                continue
+            contrib = (Xp[a:b].astype(np.float64).T @ dY[a:b].astype(np.float64)).astype(dtype)
+            if g < E:
+                dW_home[g] += contrib
+            else:
+                dW_slots[r, g - E] += contrib
+    return dW_home, dW_slots
+
+
+def reduce_grad(slot_expert, dW_home, dW_slots, dtype=np.float64):
+    """Fold every consumed reduce-buffer slot into its home expert's gradient, then zero it.
+
+    For each expert, ranks are visited in ascending order and the running value
+    starts from the home gradient ([P2] "Memory contract": reduce_grad reads the
+    slots of all ranks, accumulates into the parameter gradient and clears the
+    consumed slots).  With dtype=float32 the additions are float32 in exactly
+    this order.  Works in place.
+    """
+    R, B = slot_expert.shape
+    E = dW_home.shape[0]
+    for e in range(E):
+        acc = None
+        for r in range(R):
+            for j in range(B):
+                if slot_expert[r, j] == e:
+                    if acc is None:
+                        acc = dW_home[e].astype(dtype)
+                    acc = (acc + dW_slots[r, j].astype(dtype)).astype(dtype)
+                    dW_slots[r, j] = 0
+        if acc is not None:
+            dW_home[e] = acc
+    return dW_home, dW_slots
+
+
+# ------------------------------------------------------------------ plain definitions
+
+def moe_forward(X, W_home, topk_idx, gates, tokens=None) -> np.ndarray:
+    """Plain MoE projection: out[r,s] = sum_k gate[r,s,k] * X[r,s] @ W[topk_idx[r,s,k]]."""
+    R, S, H = X.shape
+    K = topk_idx.shape[2]
+    Xf = X.reshape(R * S, H)
+    ids = np.asarray(topk_idx).reshape(R * S, K)
+    gf = np.asarray(gates, dtype=np.float64).reshape(R * S, K)
+    tok = np.arange(R * S) if tokens is None else np.asarray(tokens)
+    out = np.zeros((len(tok), W_home.shape[2]), dtype=np.float64)
+    for i, t in enumerate(tok):
+        x = Xf[t].astype(np.float64)
+        for k in range(K):
+            out[i] += gf[t, k] * (x @ W_home[ids[t, k]].astype(np.float64))
+    return out if tokens is not None else out.reshape(R, S, -1)
+
+
+def expert_weight_grad(X, dY_of_pair, topk_idx, E: int) -> np.ndarray:
+    """Plain expert weight gradient: dW[e] = sum over pairs (t,k) with expert e of x_t^T dy_(t,k)."""
+    R, S, H = X.shape
+    K = topk_idx.shape[2]
+    Xf = X.reshape(R * S, H).astype(np.float64)
+    ids = np.asarray(topk_idx).reshape(R * S * K)
+    dW = np.zeros((E, H, dY_of_pair.shape[1]), dtype=np.float64)
+    for e in range(E):
+        q = np.nonzero(ids == e)[0]
+        if len(q):
+            dW[e] = Xf[q // K].T @ dY_of_pair[q].astype(np.float64)
+    return dW
