@@ -1,0 +1,398 @@
+// Row-moving kernels of the balanced MoE layer on gfx950: dispatch, prefetch, combine, reduce_grad.
+//
+// All four are HBM-bound streams of 16-byte vectors ([P2] = "Moonshot open-sources
+// MoonEP: an expert-parallel communication library for MoE training",
+// umios.umi6.com, sections "Core technique" and "Memory contract and weight
+// layout"):
+//   dispatch    one wave per token: the row is read once into registers and
+//               stored K times (fused permute into the expert-grouped buffer).
+//   prefetch    persistent blocks copy every used slot's [H,Hp] expert matrix.
+//   combine     one thread per 16 bytes of input row: K gathers, fp32 FMA in k order.
+//   reduce_grad persistent blocks fold each expert's slot gradients (ranks in
+//               ascending order) into the home gradient and zero the slots.
+#include "block_scan.h"
+#include "moonep_common.h"
+
+namespace moonep {
+namespace {
+
+// ------------------------------------------------------------------ dispatch
+
+constexpr int kDispatchThreads = 256;
+constexpr int kDispatchChunk = 8;  // 16-byte vectors held per lane at a time
+
+template <typename V>
+__global__ __launch_bounds__(kDispatchThreads) void dispatch_rows(const V* __restrict__ X,
+                                                                  const int32_t* __restrict__ dest,
+                                                                  V* __restrict__ Xp, int64_t tokens, int K,
+                                                                  int nvec) {
+  const int lane = threadIdx.x & 63;
+  const int64_t tok = (int64_t)blockIdx.x * (kDispatchThreads / 64) + (threadIdx.x >> 6);
+  if (tok >= tokens) return;
+  const V* src = X + tok * nvec;
+  const int32_t* dk = dest + tok * K;
+  for (int v0 = 0; v0 < nvec; v0 += 64 * kDispatchChunk) {
+    V r[kDispatchChunk];
+#pragma unroll
+    for (int c = 0; c < kDispatchChunk; ++c) {
+      const int v = v0 + c * 64 + lane;
+      if (v < nvec) r[c] = src[v];
+    }
+    for (int k = 0; k < K; ++k) {
+      const int32_t d = dk[k];
+      if (d < 0) continue;
+      V* dst = Xp + (int64_t)d * nvec;
+#pragma unroll
+      for (int c = 0; c < kDispatchChunk; ++c) {
+        const int v = v0 + c * 64 + lane;
+        if (v < nvec) __builtin_nontemporal_store(r[c], dst + v);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ prefetch
+
+constexpr int kCopyThreads = 256;
+constexpr int kCopyUnroll = 4;
+constexpr int kMaxSlots = 32768;
+
+template <typename V>
+__global__ __launch_bounds__(kCopyThreads) void prefetch_slots(const V* __restrict__ W_home,
+                                                               const int32_t* __restrict__ slot_expert,
+                                                               V* __restrict__ W_slots, int RB, int E,
+                                                               int64_t nvec) {
+  extern __shared__ int32_t used[];  // [RB] used slots, ascending
+  __shared__ int32_t wsum[kCopyThreads / 64];
+  const int n = block_compact(
+      RB, [&](int s) {
+        const int e = slot_expert[s];
+        return e >= 0 && e < E;
+      },
+      used, wsum);
+  const int64_t per_item = (int64_t)kCopyThreads * kCopyUnroll;
+  const int64_t chunks = (nvec + per_item - 1) / per_item;
+  const int64_t items = (int64_t)n * chunks;
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const int s = used[it / chunks];
+    const int64_t c = it % chunks;
+    const int e = slot_expert[s];
+    const V* src = W_home + (int64_t)e * nvec;
+    V* dst = W_slots + (int64_t)s * nvec;
+    V r[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const int64_t v = c * per_item + u * kCopyThreads + threadIdx.x;
+      if (v < nvec) r[u] = src[v];
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const int64_t v = c * per_item + u * kCopyThreads + threadIdx.x;
+      if (v < nvec) dst[v] = r[u];
+    }
+  }
+}
+
+// ------------------------------------------------------------------ combine
+
+template <int VEC>
+struct InVec;
+template <>
+struct InVec<8> {  // 8 bf16
+  static __device__ __forceinline__ void load(const void* p, float* f) {
+    const u32x4 q = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(q[i] << 16);
+      f[2 * i + 1] = __uint_as_float(q[i] & 0xffff0000u);
+    }
+  }
+};
+template <>
+struct InVec<4> {  // 4 f32
+  static __device__ __forceinline__ void load(const void* p, float* f) {
+    const f32x4 q = *reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = q[i];
+  }
+};
+
+constexpr int kCombineThreads = 256;
+
+// VEC elements of 16 bytes per thread; ESZ = element bytes of Yp.
+template <int VEC, int ESZ>
+__global__ __launch_bounds__(kCombineThreads) void combine_vec(const char* __restrict__ Yp,
+                                                               const int32_t* __restrict__ dest,
+                                                               const float* __restrict__ gates,
+                                                               float* __restrict__ out, int64_t tokens, int K,
+                                                               int D) {
+  const int nchunk = D / VEC;
+  const int64_t item = (int64_t)blockIdx.x * kCombineThreads + threadIdx.x;
+  if (item >= tokens * nchunk) return;
+  const int64_t tok = item / nchunk;
+  const int c = (int)(item % nchunk);
+  float acc[VEC];
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
+  for (int k = 0; k < K; ++k) {
+    const int32_t d = dest[tok * K + k];
+    if (d < 0) continue;
+    const float g = gates[tok * K + k];
+    float y[VEC];
+    InVec<VEC>::load(Yp + ((int64_t)d * D + (int64_t)c * VEC) * ESZ, y);
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) acc[i] = __builtin_fmaf(g, y[i], acc[i]);
+  }
+  f32x4* o = reinterpret_cast<f32x4*>(out + tok * D + (int64_t)c * VEC);
+#pragma unroll
+  for (int i = 0; i < VEC / 4; ++i) {
+    f32x4 q = {acc[4 * i], acc[4 * i + 1], acc[4 * i + 2], acc[4 * i + 3]};
+    __builtin_nontemporal_store(q, o + i);
+  }
+}
+
+// Scalar fallback for widths that are not a multiple of 16 bytes.
+template <typename T>
+__global__ __launch_bounds__(kCombineThreads) void combine_scalar(const T* __restrict__ Yp,
+                                                                  const int32_t* __restrict__ dest,
+                                                                  const float* __restrict__ gates,
+                                                                  float* __restrict__ out, int64_t tokens, int K,
+                                                                  int D) {
+  const int64_t item = (int64_t)blockIdx.x * kCombineThreads + threadIdx.x;
+  if (item >= tokens * D) return;
+  const int64_t tok = item / D;
+  const int c = (int)(item % D);
+  float acc = 0.f;
+  for (int k = 0; k < K; ++k) {
+    const int32_t d = dest[tok * K + k];
+    if (d < 0) continue;
+    float y;
+    if constexpr (sizeof(T) == 2)
+      y = bf16_to_f32(reinterpret_cast<const uint16_t*>(Yp)[(int64_t)d * D + c]);
+    else
+      y = reinterpret_cast<const float*>(Yp)[(int64_t)d * D + c];
+    acc = __builtin_fmaf(gates[tok * K + k], y, acc);
+  }
+  out[tok * D + c] = acc;
+}
+
+// ------------------------------------------------------------------ reduce_grad
+
+constexpr int kReduceThreads = 256;
+constexpr int kReduceUnroll = 4;
+constexpr size_t kMaxDynLds = 160 * 1024 - 1024;
+
+__global__ __launch_bounds__(kReduceThreads) void reduce_grad_kernel(const int32_t* __restrict__ slot_expert,
+                                                                     f32x4* __restrict__ dW_home,
+                                                                     f32x4* __restrict__ dW_slots, int R, int B,
+                                                                     int E, int64_t nvec) {
+  extern __shared__ int32_t sh[];
+  const int RB = R * B;
+  int32_t* sslot = sh;            // [RB] expert held by each slot, -1 unused
+  int32_t* flag = sslot + RB;     // [E]  expert has at least one copy
+  int32_t* elist = flag + E;      // [E]  experts with copies, ascending
+  int32_t* loff = elist + E;      // [E+1] CSR offsets into lslot
+  int32_t* lslot = loff + E + 1;  // [RB] slots of each listed expert, ranks ascending
+  __shared__ int32_t wsum[kReduceThreads / 64];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) flag[e] = 0;
+  __syncthreads();
+  for (int s = threadIdx.x; s < RB; s += blockDim.x) {
+    const int e = slot_expert[s];
+    const bool ok = e >= 0 && e < E;
+    sslot[s] = ok ? e : -1;
+    if (ok) flag[e] = 1;  // every writer stores the same value
+  }
+  __syncthreads();
+  const int n = block_compact(E, [&](int e) { return flag[e] != 0; }, elist, wsum);
+  // slots of each listed expert in ascending (rank, j) order; a rank holds an expert at most once
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const int e = elist[i];
+    int c = 0;
+    for (int s = 0; s < RB; ++s) c += sslot[s] == e;
+    loff[i] = c;
+  }
+  __syncthreads();
+  const int total = block_excl_scan(loff, n, wsum);
+  if (threadIdx.x == 0) loff[n] = total;
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const int e = elist[i];
+    int p = loff[i];
+    for (int s = 0; s < RB; ++s)
+      if (sslot[s] == e) lslot[p++] = s;
+  }
+  __syncthreads();
+  const int64_t per_item = (int64_t)kReduceThreads * kReduceUnroll;
+  const int64_t chunks = (nvec + per_item - 1) / per_item;
+  const int64_t items = (int64_t)n * chunks;
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const int i = (int)(it / chunks);
+    const int64_t c = it % chunks;
+    const int e = elist[i];
+    f32x4 acc[kReduceUnroll];
+    f32x4* home = dW_home + (int64_t)e * nvec;
+#pragma unroll
+    for (int u = 0; u < kReduceUnroll; ++u) {
+      const int64_t v = c * per_item + u * kReduceThreads + threadIdx.x;
+      if (v < nvec) acc[u] = home[v];
+    }
+    for (int p = loff[i]; p < loff[i + 1]; ++p) {
+      f32x4* sl = dW_slots + (int64_t)lslot[p] * nvec;
+#pragma unroll
+      for (int u = 0; u < kReduceUnroll; ++u) {
+        const int64_t v = c * per_item + u * kReduceThreads + threadIdx.x;
+        if (v < nvec) {
+          const f32x4 x = sl[v];
+          acc[u][0] = acc[u][0] + x[0];
+          acc[u][1] = acc[u][1] + x[1];
+          acc[u][2] = acc[u][2] + x[2];
+          acc[u][3] = acc[u][3] + x[3];
+          sl[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kReduceUnroll; ++u) {
+      const int64_t v = c * per_item + u * kReduceThreads + threadIdx.x;
+      if (v < nvec) home[v] = acc[u];
+    }
+  }
+}
+
+// scalar fallback: one thread per element (H*Hp not a multiple of 4)
+__global__ __launch_bounds__(kReduceThreads) void reduce_grad_scalar(const int32_t* __restrict__ slot_expert,
+                                                                     float* __restrict__ dW_home,
+                                                                     float* __restrict__ dW_slots, int R, int B,
+                                                                     int E, int64_t nel) {
+  const int64_t item = (int64_t)blockIdx.x * kReduceThreads + threadIdx.x;
+  if (item >= (int64_t)E * nel) return;
+  const int e = (int)(item / nel);
+  const int64_t x = item % nel;
+  bool any = false;
+  float acc = 0.f;
+  for (int r = 0; r < R; ++r)
+    for (int j = 0; j < B; ++j)
+      if (slot_expert[r * B + j] == e) {
+        if (!any) acc = dW_home[(int64_t)e * nel + x];
+        any = true;
+        float* sl = dW_slots + ((int64_t)r * B + j) * nel + x;
+        acc = acc + *sl;
+        *sl = 0.f;
+      }
+  if (any) dW_home[(int64_t)e * nel + x] = acc;
+}
+
+}  // namespace
+}  // namespace moonep
+
+using namespace moonep;
+
+extern "C" int moonep_dispatch(moonep_dims d, int32_t H, moonep_dtype t, const void* X, const int32_t* dest_idx,
+                               void* Xp, moonep_stream stream) {
+  if (int rc = check_dims(d, "moonep_dispatch")) return rc;
+  MOONEP_REQUIRE(t == MOONEP_F32 || t == MOONEP_BF16, "moonep_dispatch: bad dtype %d", (int)t);
+  MOONEP_REQUIRE(H >= 1, "moonep_dispatch: H must be >= 1");
+  const int64_t tokens = (int64_t)d.R * d.S;
+  if (tokens == 0) return MOONEP_OK;
+  MOONEP_REQUIRE(X && dest_idx && Xp, "moonep_dispatch: null pointer");
+  const size_t row = (size_t)H * elem_bytes(t);
+  hipStream_t s = as_stream(stream);
+  const unsigned grid = ceil_div_u(tokens, kDispatchThreads / 64);
+  if (row % 16 == 0) {
+    MOONEP_REQUIRE(aligned16(X) && aligned16(Xp), "moonep_dispatch: X and Xp must be 16-byte aligned");
+    hipLaunchKernelGGL(dispatch_rows<u32x4>, dim3(grid), dim3(kDispatchThreads), 0, s,
+                       static_cast<const u32x4*>(X), dest_idx, static_cast<u32x4*>(Xp), tokens, d.K, (int)(row / 16));
+  } else if (t == MOONEP_F32) {
+    hipLaunchKernelGGL(dispatch_rows<float>, dim3(grid), dim3(kDispatchThreads), 0, s,
+                       static_cast<const float*>(X), dest_idx, static_cast<float*>(Xp), tokens, d.K, (int)H);
+  } else {
+    hipLaunchKernelGGL(dispatch_rows<uint16_t>, dim3(grid), dim3(kDispatchThreads), 0, s,
+                       static_cast<const uint16_t*>(X), dest_idx, static_cast<uint16_t*>(Xp), tokens, d.K, (int)H);
+  }
+  MOONEP_LAUNCH_CHECK("moonep_dispatch");
+  return MOONEP_OK;
+}
+
+extern "C" int moonep_prefetch(moonep_dims d, int32_t H, int32_t Hp, moonep_dtype t, const void* W_home,
+                               const int32_t* slot_expert, void* W_slots, moonep_stream stream) {
+  if (int rc = check_dims(d, "moonep_prefetch")) return rc;
+  MOONEP_REQUIRE(t == MOONEP_F32 || t == MOONEP_BF16, "moonep_prefetch: bad dtype %d", (int)t);
+  MOONEP_REQUIRE(H >= 1 && Hp >= 1, "moonep_prefetch: H and Hp must be >= 1");
+  if (d.B == 0) return MOONEP_OK;
+  MOONEP_REQUIRE((int64_t)d.R * d.B <= kMaxSlots, "moonep_prefetch: R*B exceeds %d", kMaxSlots);
+  MOONEP_REQUIRE(W_home && slot_expert && W_slots, "moonep_prefetch: null pointer");
+  const size_t mat = (size_t)H * Hp * elem_bytes(t);
+  hipStream_t s = as_stream(stream);
+  const unsigned grid = (unsigned)device_cu_count() * 4;
+  const size_t lds = (size_t)d.R * d.B * sizeof(int32_t);
+  if (lds > 65536) {
+    (void)hipFuncSetAttribute((const void*)prefetch_slots<u32x4>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    (void)hipFuncSetAttribute((const void*)prefetch_slots<uint16_t>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  }
+  if (mat % 16 == 0) {
+    MOONEP_REQUIRE(aligned16(W_home) && aligned16(W_slots), "moonep_prefetch: weights must be 16-byte aligned");
+    hipLaunchKernelGGL(prefetch_slots<u32x4>, dim3(grid), dim3(kCopyThreads), lds, s,
+                       static_cast<const u32x4*>(W_home), slot_expert, static_cast<u32x4*>(W_slots), d.R * d.B, d.E,
+                       (int64_t)(mat / 16));
+  } else {
+    hipLaunchKernelGGL(prefetch_slots<uint16_t>, dim3(grid), dim3(kCopyThreads), lds, s,
+                       static_cast<const uint16_t*>(W_home), slot_expert, static_cast<uint16_t*>(W_slots), d.R * d.B,
+                       d.E, (int64_t)(mat / 2));
+  }
+  MOONEP_LAUNCH_CHECK("moonep_prefetch");
+  return MOONEP_OK;
+}
+
+extern "C" int moonep_combine(moonep_dims d, int32_t D, moonep_dtype t, const void* Yp, const int32_t* dest_idx,
+                              const float* gates, float* out, moonep_stream stream) {
+  if (int rc = check_dims(d, "moonep_combine")) return rc;
+  MOONEP_REQUIRE(t == MOONEP_F32 || t == MOONEP_BF16, "moonep_combine: bad dtype %d", (int)t);
+  MOONEP_REQUIRE(D >= 1, "moonep_combine: D must be >= 1");
+  const int64_t tokens = (int64_t)d.R * d.S;
+  if (tokens == 0) return MOONEP_OK;
+  MOONEP_REQUIRE(Yp && dest_idx && gates && out, "moonep_combine: null pointer");
+  hipStream_t s = as_stream(stream);
+  const int vec = t == MOONEP_BF16 ? 8 : 4;
+  if (D % vec == 0 && aligned16(Yp) && aligned16(out)) {
+    const unsigned grid = ceil_div_u(tokens * (D / vec), kCombineThreads);
+    if (t == MOONEP_BF16)
+      hipLaunchKernelGGL((combine_vec<8, 2>), dim3(grid), dim3(kCombineThreads), 0, s,
+                         static_cast<const char*>(Yp), dest_idx, gates, out, tokens, d.K, (int)D);
+    else
+      hipLaunchKernelGGL((combine_vec<4, 4>), dim3(grid), dim3(kCombineThreads), 0, s,
+                         static_cast<const char*>(Yp), dest_idx, gates, out, tokens, d.K, (int)D);
+  } else {
+    const unsigned grid = ceil_div_u(tokens * D, kCombineThreads);
+    if (t == MOONEP_BF16)
+      hipLaunchKernelGGL(combine_scalar<uint16_t>, dim3(grid), dim3(kCombineThreads), 0, s,
+                         static_cast<const uint16_t*>(Yp), dest_idx, gates, out, tokens, d.K, (int)D);
+    else
+      hipLaunchKernelGGL(combine_scalar<float>, dim3(grid), dim3(kCombineThreads), 0, s,
+                         static_cast<const float*>(Yp), dest_idx, gates, out, tokens, d.K, (int)D);
+  }
+  MOONEP_LAUNCH_CHECK("moonep_combine");
+  return MOONEP_OK;
+}
+
+extern "C" int moonep_reduce_grad(moonep_dims d, int32_t H, int32_t Hp, const int32_t* slot_expert, float* dW_home,
+                                  float* dW_slots, moonep_stream stream) {
+  if (int rc = check_dims(d, "moonep_reduce_grad")) return rc;
+  MOONEP_REQUIRE(H >= 1 && Hp >= 1, "moonep_reduce_grad: H and Hp must be >= 1");
+  if (d.B == 0) return MOONEP_OK;
+  MOONEP_REQUIRE(slot_expert && dW_home && dW_slots, "moonep_reduce_grad: null pointer");
+  hipStream_t s = as_stream(stream);
+  const int64_t nel = (int64_t)H * Hp;
+  const size_t lds = ((size_t)2 * d.R * d.B + 3 * (size_t)d.E + 1) * sizeof(int32_t);
+  if (nel % 4 == 0 && lds <= kMaxDynLds && aligned16(dW_home) && aligned16(dW_slots)) {
+    if (lds > 65536)
+      (void)hipFuncSetAttribute((const void*)reduce_grad_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const unsigned grid = (unsigned)device_cu_count() * 4;
+    hipLaunchKernelGGL(reduce_grad_kernel, dim3(grid), dim3(kReduceThreads), lds, s, slot_expert,
+                       reinterpret_cast<f32x4*>(dW_home), reinterpret_cast<f32x4*>(dW_slots), d.R, d.B, d.E, nel / 4);
+  } else {
+    hipLaunchKernelGGL(reduce_grad_scalar, dim3(ceil_div_u((int64_t)d.E * nel, kReduceThreads)), dim3(kReduceThreads),
+                       0, s, slot_expert, dW_home, dW_slots, d.R, d.B, d.E, nel);
+  }
+  MOONEP_LAUNCH_CHECK("moonep_reduce_grad");
+  return MOONEP_OK;
+}

@@ -1,0 +1,91 @@
+"""Static buffers for one balanced MoE layer and the call sequence through libmoonep.
+
+Every buffer is allocated once, with shapes fixed by (R, E, B, S, K, H, Hp):
+nothing depends on the routing, so repeated passes allocate nothing and a
+pass can be captured in a HIP graph.  The forward pass is
+plan -> dispatch -> prefetch -> group GEMM -> combine; the backward pass is
+wgrad -> reduce_grad.  Each step is one C-ABI call whose kernels do all the
+work; this class only owns memory and passes pointers.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from ._lib import Dims, make_dims
+
+
+class MoeLayer:
+    def __init__(self, R, E, B, S, K, H, Hp=None, dtype=torch.bfloat16, device="cuda", backward=False,
+                 src_of_row=True):
+        self.d: Dims = make_dims(R, E, B, S, K)
+        d = self.d
+        self.H, self.Hp, self.dtype, self.device = H, Hp, dtype, device
+        i32 = dict(dtype=torch.int32, device=device)
+        N = d.N
+        # routing (inputs)
+        self.topk_idx = torch.zeros((R, S, K), **i32)
+        self.gates = torch.zeros((R, S, K), dtype=torch.float32, device=device)
+        # plan outputs
+        self.expert_counts = torch.zeros(E, **i32)
+        self.maxvio = torch.zeros(1, dtype=torch.float64, device=device)
+        self.cu_seqlens = torch.zeros((R, E + B + 1), **i32)
+        self.slot_expert = torch.full((R, max(B, 0)), -1, **i32)
+        self.dest_idx = torch.zeros((R, S, K), **i32)
+        self.src_of_row = torch.zeros(N, **i32) if src_of_row else None
+        self.stats = torch.zeros(4, **i32)
+        self.ws_plan = torch.empty(max(1, _lib.moonep_plan_workspace_bytes(d)), dtype=torch.uint8, device=device)
+        # activations
+        self.X = torch.zeros((R, S, H), dtype=dtype, device=device)
+        self.Xp = torch.empty((N, H), dtype=dtype, device=device)
+        if Hp is not None:
+            self.W_home = torch.zeros((E, H, Hp), dtype=dtype, device=device)
+            self.W_slots = torch.zeros((R, B, H, Hp), dtype=dtype, device=device)
+            self.Yp = torch.empty((N, Hp), dtype=dtype, device=device)
+            self.ws_gemm = torch.empty(max(1, _lib.moonep_group_gemm_workspace_bytes(d)), dtype=torch.uint8,
+                                       device=device)
+            self.out = torch.empty((R, S, Hp), dtype=torch.float32, device=device)
+            if backward:
+                self.dY = torch.zeros((N, Hp), dtype=dtype, device=device)
+                self.dW_home = torch.zeros((E, H, Hp), dtype=torch.float32, device=device)
+                self.dW_slots = torch.zeros((R, B, H, Hp), dtype=torch.float32, device=device)
+
+    # ---------------------------------------------------------------- steps
+    def plan(self, stream=None):
+        _lib.moonep_plan(self.d, self.topk_idx, self.expert_counts, self.maxvio, self.cu_seqlens,
+                         self.slot_expert if self.d.B > 0 else None, self.dest_idx, self.src_of_row, self.stats,
+                         self.ws_plan, stream)
+
+    def dispatch(self, stream=None):
+        _lib.moonep_dispatch(self.d, self.H, self.X, self.dest_idx, self.Xp, stream)
+
+    def prefetch(self, stream=None):
+        _lib.moonep_prefetch(self.d, self.H, self.Hp, self.W_home, self.slot_expert if self.d.B > 0 else None,
+                             self.W_slots if self.d.B > 0 else None, stream)
+
+    def group_gemm(self, stream=None):
+        _lib.moonep_group_gemm(self.d, self.H, self.Hp, self.Xp, self.W_home,
+                               self.W_slots if self.d.B > 0 else None, self.cu_seqlens, self.Yp, self.ws_gemm, stream)
+
+    def combine(self, stream=None):
+        _lib.moonep_combine(self.d, self.Hp, self.Yp, self.dest_idx, self.gates, self.out, stream)
+
+    def wgrad(self, stream=None):
+        _lib.moonep_wgrad(self.d, self.H, self.Hp, self.Xp, self.dY, self.cu_seqlens, self.dW_home,
+                          self.dW_slots if self.d.B > 0 else None, stream)
+
+    def reduce_grad(self, stream=None):
+        _lib.moonep_reduce_grad(self.d, self.H, self.Hp, self.slot_expert if self.d.B > 0 else None, self.dW_home,
+                                self.dW_slots if self.d.B > 0 else None, stream)
+
+    def forward(self, stream=None):
+        self.plan(stream)
+        self.dispatch(stream)
+        if self.Hp is not None:
+            self.prefetch(stream)
+            self.group_gemm(stream)
+            self.combine(stream)
+
+    def backward(self, stream=None):
+        self.wgrad(stream)
+        self.reduce_grad(stream)

@@ -1,0 +1,101 @@
+"""The C-ABI library loads, exports every symbol include/moonep.h declares, and rejects bad
+arguments on the host before enqueuing anything (CPU only: no call here reaches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import load_balanced_dispatch_amd as m
+from load_balanced_dispatch_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "moonep.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(moonep_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_seven_calls():
+    syms = declared_symbols()
+    for name in ("moonep_plan", "moonep_dispatch", "moonep_prefetch", "moonep_group_gemm", "moonep_combine",
+                 "moonep_wgrad", "moonep_reduce_grad"):
+        assert name in syms
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(m.LIB_PATH)
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    assert sorted(declared_symbols()) == sorted(_lib.SYMBOLS)
+
+
+def test_workspace_queries():
+    d = m.make_dims(8, 64, 8, 4096, 6)
+    assert m.moonep_plan_workspace_bytes(d) > 0
+    assert m.moonep_group_gemm_workspace_bytes(d) >= 2 * 4 * (8 * 72 + 1)
+    assert m.moonep_plan_workspace_bytes(m.make_dims(64, 384, 4, 2048, 8)) > 0
+
+
+@pytest.mark.parametrize("dims,msg", [
+    ((8, 63, 8, 16, 2), "multiple of R"),
+    ((0, 64, 8, 16, 2), "R must be"),
+    ((8, 64, -1, 16, 2), "B must be"),
+    ((8, 64, 8, -1, 2), "S must be"),
+    ((8, 64, 8, 16, 0), "K must be"),
+    ((8, 64, 8, 16, 65), "K must be"),
+    ((1024, 1024, 1, 1 << 20, 8), "2^31"),
+])
+def test_bad_dims_rejected_everywhere(dims, msg):
+    d = m.make_dims(*dims)
+    L = _lib.lib()
+    null = None
+    calls = [
+        lambda: L.moonep_plan(d, *([null] * 10)),
+        lambda: L.moonep_dispatch(d, 8, 1, null, null, null, null),
+        lambda: L.moonep_prefetch(d, 8, 8, 1, null, null, null, null),
+        lambda: L.moonep_group_gemm(d, 8, 8, 1, *([null] * 7)),
+        lambda: L.moonep_combine(d, 8, 1, null, null, null, null, null),
+        lambda: L.moonep_wgrad(d, 8, 8, 1, *([null] * 6)),
+        lambda: L.moonep_reduce_grad(d, 8, 8, null, null, null, null),
+    ]
+    for c in calls:
+        assert c() == _lib.MOONEP_EINVAL
+        assert msg in m.last_error()
+    assert m.moonep_plan_workspace_bytes(d) == 0
+
+
+def test_null_pointers_rejected():
+    d = m.make_dims(2, 4, 1, 3, 1)
+    L = _lib.lib()
+    assert L.moonep_plan(d, *([None] * 10)) == _lib.MOONEP_EINVAL
+    assert "null" in m.last_error()
+    assert L.moonep_dispatch(d, 8, 1, None, None, None, None) == _lib.MOONEP_EINVAL
+    assert L.moonep_group_gemm(d, 8, 8, 1, *([None] * 7)) == _lib.MOONEP_EINVAL
+    assert L.moonep_wgrad(d, 8, 8, 1, *([None] * 6)) == _lib.MOONEP_EINVAL
+    assert L.moonep_reduce_grad(d, 8, 8, None, None, None, None) == _lib.MOONEP_EINVAL
+
+
+def test_bad_dtype_rejected():
+    d = m.make_dims(2, 4, 1, 3, 1)
+    L = _lib.lib()
+    assert L.moonep_dispatch(d, 8, 7, None, None, None, None) == _lib.MOONEP_EINVAL
+    assert "dtype" in m.last_error()
+
+
+def test_empty_work_is_a_no_op():
+    # S == 0: nothing to move or multiply; returns OK without touching any pointer
+    d = m.make_dims(2, 4, 1, 0, 1)
+    L = _lib.lib()
+    assert L.moonep_dispatch(d, 8, 1, None, None, None, None) == _lib.MOONEP_OK
+    assert L.moonep_combine(d, 8, 1, None, None, None, None, None) == _lib.MOONEP_OK
+    assert L.moonep_group_gemm(d, 8, 8, 1, *([None] * 7)) == _lib.MOONEP_OK
+    assert L.moonep_wgrad(d, 8, 8, 1, *([None] * 6)) == _lib.MOONEP_OK
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    d = m.make_dims(2, 4, 1, 3, 1)
+    with pytest.raises(ValueError, match="device tensor"):
+        m.moonep_dispatch(d, 8, torch.zeros(6, 8), torch.zeros(6, dtype=torch.int32), torch.zeros(6, 8))

@@ -1,0 +1,351 @@
+"""Per-call parity of the HIP library against the CPU oracle on small inputs that still span
+several tiles and ragged tails (GPU).
+
+Integers and copies must match bit for bit; bf16 GEMMs |gpu-ref| <= 1e-2*(1+|ref|)
+against float64 on the bf16-rounded inputs; float32 GEMMs 1e-4*(1+|ref|); combine
+1e-5 * sum|g*y|; reduce_grad bitwise equal to float32 additions in rank order.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import layer as olayer
+from oracle import planner as oplanner
+from tests.gpu_util import (DEV, assert_gemm_close, assert_sum_close, f32, i32, np64, npi, rand_tensor, say)
+from tests.plan_checks import check_plan_invariants, random_routing
+
+pytestmark = pytest.mark.gpu
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module")
+def m():
+    import load_balanced_dispatch_amd as mod
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible GPU")
+    return mod
+
+
+def gpu_plan(m, topk, E, B, src=True):
+    topk = np.asarray(topk)
+    R, S, K = topk.shape
+    d = m.make_dims(R, E, B, S, K)
+    out = dict(
+        counts=torch.full((E,), -7, dtype=torch.int32, device=DEV),
+        maxvio=torch.full((1,), -7.0, dtype=torch.float64, device=DEV),
+        cu=torch.full((R, E + B + 1), -7, dtype=torch.int32, device=DEV),
+        slots=torch.full((R, B), -7, dtype=torch.int32, device=DEV) if B > 0 else None,
+        dest=torch.full((R, S, K), -7, dtype=torch.int32, device=DEV),
+        src=torch.full((R * S * K,), -7, dtype=torch.int32, device=DEV) if src else None,
+        stats=torch.full((4,), -7, dtype=torch.int32, device=DEV),
+    )
+    ws = torch.full((max(1, m.moonep_plan_workspace_bytes(d)),), 0xAB, dtype=torch.uint8, device=DEV)
+    m.moonep_plan(d, i32(topk), out["counts"], out["maxvio"], out["cu"], out["slots"], out["dest"], out["src"],
+                  out["stats"], ws)
+    torch.cuda.synchronize()
+    return d, out
+
+
+def assert_plan_equal(out, p, B):
+    assert npi(out["counts"]).tolist() == p.expert_counts.tolist()
+    assert float(out["maxvio"].item()) == p.maxvio  # same float64 expression on both sides
+    assert np.array_equal(npi(out["cu"]), p.cu_seqlens)
+    if B > 0:
+        assert np.array_equal(npi(out["slots"]), p.slot_expert)
+    assert np.array_equal(npi(out["dest"]), p.dest_idx)
+    if out["src"] is not None:
+        assert np.array_equal(npi(out["src"]), p.src_of_row)
+    assert npi(out["stats"]).tolist() == p.stats.tolist()
+
+
+# ------------------------------------------------------------------ planner
+
+
+@pytest.mark.parametrize("name", ["plan_example1.json", "plan_example2.json"])
+def test_plan_hand_worked_examples(m, name):
+    g = json.load(open(os.path.join(GOLD, name)))
+    say("plan golden", name)
+    _, out = gpu_plan(m, g["topk_idx"], g["E"], g["B"])
+    assert npi(out["cu"]).tolist() == g["cu_seqlens"]
+    assert npi(out["dest"]).tolist() == g["dest_idx"]
+    assert npi(out["stats"]).tolist() == g["stats"]
+    assert npi(out["slots"]).tolist() == g["slot_expert"]
+    assert abs(out["maxvio"].item() - g["maxvio_num"] / g["maxvio_den"]) < 1e-15
+
+
+def small_plan_case(seed):
+    rng = np.random.default_rng(7000 + seed)
+    R = int(rng.integers(1, 9))
+    per = int(rng.integers(1, 9))
+    E = R * per
+    K = int(rng.integers(1, min(E, 8) + 1))
+    S = int(rng.integers(1, 400))
+    B = int(rng.integers(0, per + 3))
+    return random_routing(rng, R, S, K, E, float(rng.uniform(0, 3))), E, B
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_plan_random_bit_exact(m, seed):
+    topk, E, B = small_plan_case(seed)
+    say("plan random", seed, topk.shape, E, B)
+    _, out = gpu_plan(m, topk, E, B)
+    p = oplanner.plan(topk, E, B)
+    assert_plan_equal(out, p, B)
+    if topk.size <= 4000:
+        check_plan_invariants(topk, E, B, npi(out["cu"]), npi(out["slots"]) if B else np.zeros((topk.shape[0], 0)),
+                              npi(out["dest"]), npi(out["src"]), npi(out["stats"]))
+
+
+@pytest.mark.parametrize("R,E,B,S,K", [
+    (4, 16, 4, 64, 2),       # tiny workload shape
+    (3, 12, 0, 777, 3),      # no slots: every copy is a direct read
+    (1, 5, 2, 1000, 5),      # one rank: nothing can move, K = E
+    (8, 64, 8, 2731, 6),     # several count/emit blocks with a ragged last block
+    (16, 64, 1, 300, 4),     # many ranks, one slot
+])
+def test_plan_shapes_bit_exact(m, R, E, B, S, K):
+    rng = np.random.default_rng(R * 1000 + S)
+    topk = random_routing(rng, R, S, K, E, 2.0)
+    say("plan shape", R, E, B, S, K)
+    _, out = gpu_plan(m, topk, E, B)
+    assert_plan_equal(out, oplanner.plan(topk, E, B), B)
+
+
+def test_plan_empty_routing(m):
+    say("plan empty")
+    topk = np.zeros((4, 0, 2), dtype=np.int64)
+    d = m.make_dims(4, 8, 2, 0, 2)
+    counts = torch.full((8,), -1, dtype=torch.int32, device=DEV)
+    mv = torch.full((1,), -1.0, dtype=torch.float64, device=DEV)
+    cu = torch.full((4, 11), -1, dtype=torch.int32, device=DEV)
+    slots = torch.full((4, 2), -5, dtype=torch.int32, device=DEV)
+    stats = torch.full((4,), -1, dtype=torch.int32, device=DEV)
+    ws = torch.empty(max(1, m.moonep_plan_workspace_bytes(d)), dtype=torch.uint8, device=DEV)
+    dummy = torch.zeros(1, dtype=torch.int32, device=DEV)
+    from load_balanced_dispatch_amd import _lib
+    rc = _lib.lib().moonep_plan(d, dummy.data_ptr(), counts.data_ptr(), mv.data_ptr(), cu.data_ptr(),
+                                slots.data_ptr(), dummy.data_ptr(), None, stats.data_ptr(), ws.data_ptr(),
+                                torch.cuda.current_stream().cuda_stream)
+    assert rc == 0
+    torch.cuda.synchronize()
+    assert npi(counts).tolist() == [0] * 8
+    assert mv.item() == 0.0
+    assert np.all(npi(cu) == 0)
+    assert np.all(npi(slots) == -1)
+    assert npi(stats).tolist() == [0, 0, 0, 0]
+
+
+def test_plan_counts_invalid_and_repeated_ids(m):
+    rng = np.random.default_rng(3)
+    topk = random_routing(rng, 2, 50, 3, 8, 1.0)
+    topk[0, 3, 1] = 8       # out of range
+    topk[1, 7, 0] = -2      # negative
+    topk[1, 9, 2] = topk[1, 9, 0]  # repeated within a token
+    say("plan invalid ids")
+    _, out = gpu_plan(m, topk, 8, 2)
+    assert npi(out["stats"])[3] == 3
+    dest = npi(out["dest"])
+    assert dest[0, 3, 1] == -1 and dest[1, 7, 0] == -1
+    valid = dest[dest >= 0]
+    assert len(np.unique(valid)) == len(valid) and valid.max() < topk.size
+
+
+# ------------------------------------------------------------------ dispatch / prefetch
+
+
+@pytest.mark.parametrize("dtype,H", [(torch.bfloat16, 2048), (torch.bfloat16, 7168), (torch.float32, 128),
+                                     (torch.float32, 7), (torch.bfloat16, 5)])
+def test_dispatch_bit_exact(m, dtype, H):
+    rng = np.random.default_rng(H)
+    R, E, B, S, K = 4, 16, 3, 97, 4
+    topk = random_routing(rng, R, S, K, E, 2.0)
+    p = oplanner.plan(topk, E, B)
+    X = rand_tensor((R, S, H), dtype, seed=H)
+    Xp = torch.full((R * S * K, H), float("nan"), dtype=dtype, device=DEV)
+    say("dispatch", dtype, H)
+    m.moonep_dispatch(m.make_dims(R, E, B, S, K), H, X, i32(p.dest_idx), Xp)
+    torch.cuda.synchronize()
+    ref = olayer.dispatch(X.cpu().float().numpy(), p.dest_idx)
+    assert np.array_equal(Xp.cpu().float().numpy(), ref)  # also proves every row was written (no NaN)
+
+
+@pytest.mark.parametrize("dtype,H,Hp", [(torch.bfloat16, 256, 384), (torch.float32, 24, 40), (torch.bfloat16, 3, 5)])
+def test_prefetch_bit_exact_and_unused_slots_untouched(m, dtype, H, Hp):
+    rng = np.random.default_rng(Hp)
+    R, E, B, S, K = 4, 16, 3, 64, 3
+    topk = random_routing(rng, R, S, K, E, 3.0)
+    p = oplanner.plan(topk, E, B)
+    assert p.stats[1] > 0
+    W = rand_tensor((E, H, Hp), dtype, seed=5)
+    Ws = torch.full((R, B, H, Hp), 7.0, dtype=dtype, device=DEV)
+    say("prefetch", dtype, H, Hp)
+    m.moonep_prefetch(m.make_dims(R, E, B, S, K), H, Hp, W, i32(p.slot_expert), Ws)
+    torch.cuda.synchronize()
+    ref = olayer.prefetch(W.cpu().float().numpy(), p.slot_expert, np.full((R, B, H, Hp), 7.0))
+    assert np.array_equal(Ws.cpu().float().numpy(), ref)
+
+
+# ------------------------------------------------------------------ group GEMM
+
+
+@pytest.mark.parametrize("dtype,R,E,B,S,K,H,Hp", [
+    (torch.bfloat16, 2, 4, 2, 300, 2, 192, 256),    # MFMA path: 2+ M tiles per group, partial tiles, 2 N tiles
+    (torch.bfloat16, 4, 16, 4, 160, 3, 128, 128),   # MFMA path, many small groups and slots
+    (torch.bfloat16, 3, 6, 0, 200, 2, 64, 384),     # MFMA path, no slots, direct reads
+    (torch.bfloat16, 2, 4, 1, 50, 2, 40, 72),       # generic bf16 path (H % 64 != 0)
+    (torch.float32, 4, 16, 4, 64, 2, 128, 256),     # tiny workload shape, float32
+    (torch.float32, 2, 6, 1, 37, 3, 33, 65),        # float32, ragged everything
+])
+def test_group_gemm(m, dtype, R, E, B, S, K, H, Hp):
+    rng = np.random.default_rng(S * 7 + H)
+    topk = random_routing(rng, R, S, K, E, 2.5)
+    p = oplanner.plan(topk, E, B)
+    X = rand_tensor((R, S, H), dtype, seed=11)
+    W = rand_tensor((E, H, Hp), dtype, seed=12, std=H ** -0.5)
+    Xp_ref = olayer.dispatch(X.cpu().float().numpy().astype(np.float64), p.dest_idx)
+    Ws_ref = olayer.prefetch(W.cpu().float().numpy().astype(np.float64), p.slot_expert)
+    d = m.make_dims(R, E, B, S, K)
+    Xp = torch.as_tensor(Xp_ref, dtype=torch.float32).to(dtype).to(DEV)
+    Ws = torch.as_tensor(Ws_ref, dtype=torch.float32).to(dtype).to(DEV) if B > 0 else None
+    Yp = torch.full((R * S * K, Hp), float("nan"), dtype=dtype, device=DEV)
+    ws = torch.empty(m.moonep_group_gemm_workspace_bytes(d), dtype=torch.uint8, device=DEV)
+    say("group_gemm", dtype, R, E, B, S, K, H, Hp)
+    m.moonep_group_gemm(d, H, Hp, Xp, W, Ws, i32(p.cu_seqlens), Yp, ws)
+    torch.cuda.synchronize()
+    ref = olayer.group_gemm(Xp_ref, W.cpu().float().numpy().astype(np.float64), Ws_ref, p.cu_seqlens, S * K)
+    rel = 1e-2 if dtype == torch.bfloat16 else 1e-4
+    assert_gemm_close(np64(Yp), ref, rel, "group_gemm")
+
+
+# ------------------------------------------------------------------ combine
+
+
+@pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 1408), (torch.bfloat16, 2048), (torch.float32, 256),
+                                     (torch.bfloat16, 13), (torch.float32, 6)])
+def test_combine(m, dtype, D):
+    rng = np.random.default_rng(D)
+    R, E, B, S, K = 4, 16, 4, 150, 4
+    topk = random_routing(rng, R, S, K, E, 2.0)
+    p = oplanner.plan(topk, E, B)
+    Yp = rand_tensor((R * S * K, D), dtype, seed=D)
+    gates = rng.dirichlet(np.ones(K), size=(R, S)).astype(np.float32)
+    out = torch.full((R, S, D), float("nan"), dtype=torch.float32, device=DEV)
+    say("combine", dtype, D)
+    m.moonep_combine(m.make_dims(R, E, B, S, K), D, Yp, i32(p.dest_idx), f32(gates), out)
+    torch.cuda.synchronize()
+    y = np64(Yp)
+    ref = olayer.combine(y, p.dest_idx, gates)
+    scale = olayer.combine_abs(y, p.dest_idx, gates)
+    assert_sum_close(np64(out), ref, scale, 1e-5, "combine")
+
+
+def test_combine_dispatch_round_trip(m):
+    # combine(dispatch(X)) = X * sum_k gates at the [S, H] shape
+    rng = np.random.default_rng(1)
+    R, E, B, S, K, H = 4, 16, 4, 128, 2, 2048
+    topk = random_routing(rng, R, S, K, E, 2.0)
+    p = oplanner.plan(topk, E, B)
+    d = m.make_dims(R, E, B, S, K)
+    X = rand_tensor((R, S, H), torch.bfloat16, seed=2)
+    gates = rng.dirichlet(np.ones(K), size=(R, S)).astype(np.float32)
+    Xp = torch.empty((R * S * K, H), dtype=torch.bfloat16, device=DEV)
+    out = torch.empty((R, S, H), dtype=torch.float32, device=DEV)
+    say("round trip")
+    m.moonep_dispatch(d, H, X, i32(p.dest_idx), Xp)
+    m.moonep_combine(d, H, Xp, i32(p.dest_idx), f32(gates), out)
+    torch.cuda.synchronize()
+    x = np64(X)
+    ref = x * gates.astype(np.float64).sum(-1, keepdims=True)
+    assert_sum_close(np64(out), ref, np.abs(ref) + 1e-30, 1e-5, "round trip")
+
+
+# ------------------------------------------------------------------ wgrad / reduce_grad
+
+
+@pytest.mark.parametrize("dtype,R,E,B,S,K,H,Hp", [
+    (torch.bfloat16, 2, 4, 2, 300, 2, 256, 256),    # MFMA path, several 64-row chunks, ragged segments
+    (torch.bfloat16, 4, 8, 1, 100, 3, 512, 128),    # MFMA path with direct reads (B=1)
+    (torch.bfloat16, 3, 6, 0, 90, 2, 256, 384),     # MFMA path, no slots
+    (torch.bfloat16, 2, 4, 1, 40, 2, 40, 72),       # generic bf16
+    (torch.float32, 4, 16, 4, 64, 2, 128, 256),     # float32
+])
+def test_wgrad_accumulates(m, dtype, R, E, B, S, K, H, Hp):
+    rng = np.random.default_rng(S + H)
+    topk = random_routing(rng, R, S, K, E, 2.5)
+    p = oplanner.plan(topk, E, B)
+    N = R * S * K
+    Xp = rand_tensor((N, H), dtype, seed=21)
+    dY = rand_tensor((N, Hp), dtype, seed=22)
+    init_h = np.asarray(rand_tensor((E, H, Hp), torch.float32, seed=23).cpu(), dtype=np.float64)
+    init_s = np.asarray(rand_tensor((R, B, H, Hp), torch.float32, seed=24).cpu(), dtype=np.float64)
+    dWh = f32(init_h)
+    dWs = f32(init_s) if B > 0 else None
+    say("wgrad", dtype, R, E, B, S, K, H, Hp)
+    m.moonep_wgrad(m.make_dims(R, E, B, S, K), H, Hp, Xp, dY, i32(p.cu_seqlens), dWh, dWs)
+    torch.cuda.synchronize()
+    rh, rs = init_h.copy(), init_s.copy()
+    olayer.wgrad(np64(Xp), np64(dY), p.cu_seqlens, S * K, rh, rs)
+    rel = 1e-2 if dtype == torch.bfloat16 else 1e-4
+    assert_gemm_close(np64(dWh), rh, rel, "wgrad home")
+    if B > 0:
+        assert_gemm_close(np64(dWs), rs, rel, "wgrad slots")
+        # slots no group used keep their initial contents exactly
+        for r in range(R):
+            for j in range(B):
+                if p.cu_seqlens[r, E + j + 1] == p.cu_seqlens[r, E + j]:
+                    assert np.array_equal(np64(dWs[r, j]), init_s[r, j])
+
+
+@pytest.mark.parametrize("R,E,B,H,Hp", [(8, 64, 8, 64, 44), (4, 16, 4, 3, 5), (8, 32, 4, 128, 256)])
+def test_reduce_grad_rank_order_bitwise(m, R, E, B, H, Hp):
+    rng = np.random.default_rng(E)
+    S, K = 80, 4
+    topk = random_routing(rng, R, S, K, E, 3.0)
+    p = oplanner.plan(topk, E, B)
+    assert p.stats[1] > 0
+    hs = rand_tensor((E, H, Hp), torch.float32, seed=31)
+    ss = rand_tensor((R, B, H, Hp), torch.float32, seed=32) * 1e3
+    ref_h32 = hs.cpu().numpy().copy()
+    ref_s32 = ss.cpu().numpy().copy()
+    olayer.reduce_grad(p.slot_expert, ref_h32, ref_s32, dtype=np.float32)
+    ref_h64 = hs.cpu().numpy().astype(np.float64)
+    ref_s64 = ss.cpu().numpy().astype(np.float64)
+    scale_h = np.abs(ref_h64).copy()
+    olayer.reduce_grad(p.slot_expert, ref_h64, ref_s64.copy())
+    sabs = np.abs(ss.cpu().numpy().astype(np.float64))
+    olayer.reduce_grad(p.slot_expert, scale_h, sabs)
+    say("reduce_grad", R, E, B, H, Hp)
+    m.moonep_reduce_grad(m.make_dims(R, E, B, S, K), H, Hp, i32(p.slot_expert), hs, ss)
+    torch.cuda.synchronize()
+    assert np.array_equal(hs.cpu().numpy(), ref_h32)  # float32, ranks ascending, bit for bit
+    assert np.array_equal(ss.cpu().numpy(), ref_s32)  # consumed slots zero, unused slots untouched
+    assert_sum_close(hs.cpu().numpy(), ref_h64, scale_h, 1e-5, "reduce_grad vs float64")
+
+
+# ------------------------------------------------------------------ tiny workload end to end
+
+
+def test_tiny_workload_forward_matches_plain_moe(m):
+    from synthetic import WORKLOADS
+    from synthetic.router import layer_inputs
+    wl = WORKLOADS["tiny_f32"]
+    inp = layer_inputs(wl, seed=0, device="cpu")
+    L = m.MoeLayer(wl.R, wl.E, wl.B, wl.S, wl.K, wl.H, wl.Hp, dtype=torch.float32)
+    L.topk_idx.copy_(torch.as_tensor(inp["topk_idx"]))
+    L.gates.copy_(torch.as_tensor(inp["gates"]))
+    L.X.copy_(inp["X"])
+    L.W_home.copy_(inp["W_home"])
+    say("tiny workload forward")
+    L.forward()
+    torch.cuda.synchronize()
+    p = oplanner.plan(inp["topk_idx"], wl.E, wl.B)
+    assert np.array_equal(npi(L.cu_seqlens), p.cu_seqlens)
+    assert np.array_equal(npi(L.dest_idx), p.dest_idx)
+    x = inp["X"].numpy().astype(np.float64)
+    w = inp["W_home"].numpy().astype(np.float64)
+    ref = olayer.moe_forward(x, w, inp["topk_idx"], inp["gates"])
+    assert_gemm_close(np64(L.out), ref, 1e-4, "tiny forward")
