@@ -45,6 +45,10 @@ class Dims(ctypes.Structure):
 
 
 def _load():
+    # torch must bring in its HIP runtime first: libmoonep.so then binds to that same
+    # libamdhip64 (same soname) instead of loading a second runtime from /opt/rocm,
+    # and two HIP runtimes in one process leave the library's launches without a device.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with `python -m load_balanced_dispatch_amd.build`")
     lib = ctypes.CDLL(LIB_PATH)

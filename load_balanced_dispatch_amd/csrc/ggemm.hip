@@ -13,7 +13,8 @@
 //     (m-tile, n-tile) list; tile ids are remapped so the blocks of one XCD
 //     (workgroups are dealt to the 8 XCDs round-robin) take consecutive tiles,
 //     which share the same expert weights and token rows in that XCD's L2.
-//     Block tile 256 x 128 x 64, four waves of 128 x 64, MFMA 32x32x16 bf16.
+//     Block tile 256 x 128 x 32, four waves of 128 x 64, MFMA 32x32x16 bf16,
+//     two blocks per CU so one block's global loads overlap the other's MFMAs.
 //     Tiles go global -> registers -> LDS (double-buffered); the activation
 //     operand is read with ds_read_b128 (k contiguous), the weight operand --
 //     whose k runs along LDS rows -- with ds_read_b64_tr_b16.  A wave skips
@@ -106,6 +107,7 @@ struct FwdCfg {
   static constexpr int WN = BN / 2;
   static constexpr int TM = 4;         // 128 rows per wave / 32
   static constexpr int TN = WN / 32;
+  static constexpr int KK = BK / 16;   // MFMA k-steps per stage
   static constexpr int A_CPR = BK / 8;  // 16-byte chunks per A row
   static constexpr int B_CPR = BN / 8;  // 16-byte chunks per B row
   static constexpr int A_VEC = BM * BK / 8 / 256;  // 16-byte vectors per thread per stage
@@ -119,16 +121,17 @@ struct FwdCfg {
   static_assert(4 * 32 * SP <= LDS_ELEMS, "epilogue staging must fit in the stage buffers");
 };
 
+// Two blocks per CU (about 60 KB of LDS and <= 256 registers each), so one
+// block's global-load wait overlaps the other's MFMAs.
 template <int BN, int BK>
-__global__ __launch_bounds__(256) void ggemm_bf16(const uint16_t* __restrict__ Xp, const uint16_t* __restrict__ W_home,
-                                                  const uint16_t* __restrict__ W_slots,
-                                                  const int32_t* __restrict__ cu, const int32_t* __restrict__ tstart,
-                                                  uint16_t* __restrict__ Yp, int R, int E, int B, int P, int H,
-                                                  int Hp) {
+__global__ __launch_bounds__(256, 2) void ggemm_bf16(const uint16_t* __restrict__ Xp,
+                                                     const uint16_t* __restrict__ W_home,
+                                                     const uint16_t* __restrict__ W_slots,
+                                                     const int32_t* __restrict__ cu,
+                                                     const int32_t* __restrict__ tstart, uint16_t* __restrict__ Yp,
+                                                     int R, int E, int B, int P, int H, int Hp) {
   using C = FwdCfg<BN, BK>;
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
-  auto As = [&](int buf) { return lds + buf * C::A_STAGE; };
-  auto Bs = [&](int buf) { return lds + 2 * C::A_STAGE + buf * C::B_STAGE; };
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int wm = w >> 1, wn = w & 1;
   const int G = E + B, G1 = G + 1, NG = R * G;
@@ -140,6 +143,8 @@ __global__ __launch_bounds__(256) void ggemm_bf16(const uint16_t* __restrict__ X
   // this thread's slice of each stage: A row a_r + i*A_ROWS, chunk a_c; B row b_r + i*B_ROWS, chunk b_c
   const int a_r = t / C::A_CPR, a_c = t % C::A_CPR;
   const int b_r = t / C::B_CPR, b_c = t % C::B_CPR;
+  uint16_t* const a_st = lds + a_r * C::LDA + a_c * 8;                  // + buf*A_STAGE + i*A_ROWS*LDA
+  uint16_t* const b_st = lds + 2 * C::A_STAGE + b_r * C::LDB + b_c * 8;  // + buf*B_STAGE + i*B_ROWS*LDB
 
   for (int tile = vb; tile < total; tile += nblk) {
     const int mt = tile / NT, nt = tile % NT;
@@ -151,29 +156,38 @@ __global__ __launch_bounds__(256) void ggemm_bf16(const uint16_t* __restrict__ X
     const int64_t row0 = (int64_t)r * P + c0 + mo;
     const uint16_t* Wg = g < E ? W_home + (int64_t)g * H * Hp : W_slots + ((int64_t)r * B + (g - E)) * H * Hp;
     const int n0 = nt * BN;
-    // valid 32-row strips of this wave
-    const int strips = min(C::TM, max(0, (rows - wm * 128 + 31) / 32));
+    const int strips = min(C::TM, max(0, (rows - wm * 128 + 31) / 32));  // valid 32-row strips of this wave
+
+    // global sources; rows past the group end repeat the last valid row (their results are dropped)
     const uint16_t* a_base = Xp + row0 * H + a_c * 8;
-    const uint16_t* b_base = Wg + (int64_t)b_r * Hp + n0 + b_c * 8;
+    int a_off[C::A_VEC];
+#pragma unroll
+    for (int i = 0; i < C::A_VEC; ++i) a_off[i] = min(a_r + i * C::A_ROWS, rows - 1) * H;
+    const uint16_t* b_src = Wg + (int64_t)b_r * Hp + n0 + b_c * 8;
 
     u32x4 ra[C::A_VEC], rb[C::B_VEC];
     auto gload = [&](int kt) {
 #pragma unroll
-      for (int i = 0; i < C::A_VEC; ++i) {
-        const int row = min(a_r + i * C::A_ROWS, rows - 1);  // rows past the group end repeat a valid row
-        ra[i] = *reinterpret_cast<const u32x4*>(a_base + (int64_t)row * H + kt * BK);
-      }
+      for (int i = 0; i < C::A_VEC; ++i) ra[i] = *reinterpret_cast<const u32x4*>(a_base + a_off[i] + kt * BK);
 #pragma unroll
       for (int i = 0; i < C::B_VEC; ++i)
-        rb[i] = *reinterpret_cast<const u32x4*>(b_base + ((int64_t)kt * BK + i * C::B_ROWS) * Hp);
+        rb[i] = *reinterpret_cast<const u32x4*>(b_src + ((int64_t)kt * BK + i * C::B_ROWS) * Hp);
     };
     auto sstore = [&](int buf) {
 #pragma unroll
       for (int i = 0; i < C::A_VEC; ++i)
-        *reinterpret_cast<u32x4*>(As(buf) + (a_r + i * C::A_ROWS) * C::LDA + a_c * 8) = ra[i];
+        *reinterpret_cast<u32x4*>(a_st + buf * C::A_STAGE + i * C::A_ROWS * C::LDA) = ra[i];
 #pragma unroll
       for (int i = 0; i < C::B_VEC; ++i)
-        *reinterpret_cast<u32x4*>(Bs(buf) + (b_r + i * C::B_ROWS) * C::LDB + b_c * 8) = rb[i];
+        *reinterpret_cast<u32x4*>(b_st + buf * C::B_STAGE + i * C::B_ROWS * C::LDB) = rb[i];
+    };
+    auto frags = [&](int buf, int kk, bf16x8 (&a)[C::TM], bf16x8 (&b)[C::TN]) {
+      const uint16_t* As = lds + buf * C::A_STAGE;
+      const uint16_t* Bs = lds + 2 * C::A_STAGE + buf * C::B_STAGE;
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) b[j] = operand_rows_k(Bs, C::LDB, kk * 16, wn * C::WN + j * 32, lane);
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i) a[i] = operand_cols_k(As, C::LDA, wm * 128 + i * 32, kk * 16, lane);
     };
 
     f32x16 acc[C::TM][C::TN];
@@ -189,18 +203,14 @@ __global__ __launch_bounds__(256) void ggemm_bf16(const uint16_t* __restrict__ X
       const int buf = kt & 1;
       if (kt + 1 < KT) gload(kt + 1);
 #pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
-        bf16x8 b[C::TN];
+      for (int kk = 0; kk < C::KK; ++kk) {
+        bf16x8 a[C::TM], b[C::TN];
+        frags(buf, kk, a, b);
 #pragma unroll
-        for (int j = 0; j < C::TN; ++j) b[j] = operand_rows_k(Bs(buf), C::LDB, kk * 16, wn * C::WN + j * 32, lane);
+        for (int i = 0; i < C::TM; ++i)
+          if (i < strips)
 #pragma unroll
-        for (int i = 0; i < C::TM; ++i) {
-          if (i < strips) {
-            const bf16x8 a = operand_cols_k(As(buf), C::LDA, wm * 128 + i * 32, kk * 16, lane);
-#pragma unroll
-            for (int j = 0; j < C::TN; ++j) acc[i][j] = mfma32(a, b[j], acc[i][j]);
-          }
-        }
+            for (int j = 0; j < C::TN; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
       }
       if (kt + 1 < KT) sstore(buf ^ 1);
       __syncthreads();
@@ -334,13 +344,14 @@ extern "C" int moonep_group_gemm(moonep_dims d, int32_t H, int32_t Hp, moonep_dt
                  "moonep_group_gemm: workspace must be 256-byte aligned");
   MOONEP_REQUIRE(n_groups(d) < (int64_t(1) << 30), "moonep_group_gemm: too many groups");
   hipStream_t s = as_stream(stream);
+  clear_stale_error();
   int32_t* t256 = static_cast<int32_t*>(workspace);
   int32_t* t64 = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
                                             align256((size_t)(n_groups(d) + 1) * sizeof(int32_t)));
   hipLaunchKernelGGL(ggemm_tiles, dim3(1), dim3(1024), 0, s, cu_seqlens, d.R, d.E, d.B, t256, t64);
   MOONEP_LAUNCH_CHECK("moonep_group_gemm/tiles");
   const int cus = device_cu_count();
-  const bool mfma = t == MOONEP_BF16 && H % 64 == 0 && Hp % 128 == 0 && aligned16(Xp) &&
+  const bool mfma = t == MOONEP_BF16 && H % 32 == 0 && Hp % 128 == 0 && aligned16(Xp) &&
                     aligned16(W_home) && (d.B == 0 || aligned16(W_slots));
   if (mfma) {
     const auto* x = static_cast<const uint16_t*>(Xp);
@@ -348,8 +359,8 @@ extern "C" int moonep_group_gemm(moonep_dims d, int32_t H, int32_t Hp, moonep_dt
     const auto* ws = static_cast<const uint16_t*>(W_slots);
     auto* y = static_cast<uint16_t*>(Yp);
     const int P = d.S * d.K;
-    hipLaunchKernelGGL((ggemm_bf16<128, 64>), dim3(cus), dim3(256), 0, s, x, wh, ws, cu_seqlens, t256, y, d.R, d.E,
-                       d.B, P, H, Hp);
+    hipLaunchKernelGGL((ggemm_bf16<128, 32>), dim3(2 * cus), dim3(256), 0, s, x, wh, ws, cu_seqlens, t256, y, d.R,
+                       d.E, d.B, P, H, Hp);
   } else if (t == MOONEP_BF16) {
     hipLaunchKernelGGL(ggemm_generic<uint16_t>, dim3(cus * 4), dim3(256), 0, s, static_cast<const uint16_t*>(Xp),
                        static_cast<const uint16_t*>(W_home), static_cast<const uint16_t*>(W_slots), cu_seqlens, t64,

@@ -23,6 +23,10 @@ void set_error(const char* fmt, ...);
     }                                      \
   } while (0)
 
+// Clears an error left on this thread by an earlier HIP call made by someone else,
+// so that MOONEP_LAUNCH_CHECK reports only this library's launches.
+inline void clear_stale_error() { (void)hipGetLastError(); }
+
 #define MOONEP_LAUNCH_CHECK(what)                                                       \
   do {                                                                                  \
     hipError_t e_ = hipGetLastError();                                                  \
@@ -58,12 +62,12 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-// float -> bf16, round to nearest even (inputs are finite here; NaN keeps a quiet payload).
+// float -> bf16 with the hardware conversion (v_cvt_pk_bf16_f32: round to nearest even).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  const __bf16 h = (__bf16)f;
+  uint16_t u;
+  __builtin_memcpy(&u, &h, 2);
+  return u;
 }
 
 }  // namespace moonep

@@ -297,6 +297,7 @@ extern "C" int moonep_dispatch(moonep_dims d, int32_t H, moonep_dtype t, const v
   MOONEP_REQUIRE(X && dest_idx && Xp, "moonep_dispatch: null pointer");
   const size_t row = (size_t)H * elem_bytes(t);
   hipStream_t s = as_stream(stream);
+  clear_stale_error();
   const unsigned grid = ceil_div_u(tokens, kDispatchThreads / 64);
   if (row % 16 == 0) {
     MOONEP_REQUIRE(aligned16(X) && aligned16(Xp), "moonep_dispatch: X and Xp must be 16-byte aligned");
@@ -323,6 +324,7 @@ extern "C" int moonep_prefetch(moonep_dims d, int32_t H, int32_t Hp, moonep_dtyp
   MOONEP_REQUIRE(W_home && slot_expert && W_slots, "moonep_prefetch: null pointer");
   const size_t mat = (size_t)H * Hp * elem_bytes(t);
   hipStream_t s = as_stream(stream);
+  clear_stale_error();
   const unsigned grid = (unsigned)device_cu_count() * 4;
   const size_t lds = (size_t)d.R * d.B * sizeof(int32_t);
   if (lds > 65536) {
@@ -352,6 +354,7 @@ extern "C" int moonep_combine(moonep_dims d, int32_t D, moonep_dtype t, const vo
   if (tokens == 0) return MOONEP_OK;
   MOONEP_REQUIRE(Yp && dest_idx && gates && out, "moonep_combine: null pointer");
   hipStream_t s = as_stream(stream);
+  clear_stale_error();
   const int vec = t == MOONEP_BF16 ? 8 : 4;
   if (D % vec == 0 && aligned16(Yp) && aligned16(out)) {
     const unsigned grid = ceil_div_u(tokens * (D / vec), kCombineThreads);
@@ -381,6 +384,7 @@ extern "C" int moonep_reduce_grad(moonep_dims d, int32_t H, int32_t Hp, const in
   if (d.B == 0) return MOONEP_OK;
   MOONEP_REQUIRE(slot_expert && dW_home && dW_slots, "moonep_reduce_grad: null pointer");
   hipStream_t s = as_stream(stream);
+  clear_stale_error();
   const int64_t nel = (int64_t)H * Hp;
   const size_t lds = ((size_t)2 * d.R * d.B + 3 * (size_t)d.E + 1) * sizeof(int32_t);
   if (nel % 4 == 0 && lds <= kMaxDynLds && aligned16(dW_home) && aligned16(dW_slots)) {

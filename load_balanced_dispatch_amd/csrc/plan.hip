@@ -432,6 +432,7 @@ extern "C" int moonep_plan(moonep_dims d, const int32_t* topk_idx, int32_t* expe
   MOONEP_REQUIRE(N == 0 || (topk_idx && dest_idx), "moonep_plan: null topk_idx or dest_idx");
   MOONEP_REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, "moonep_plan: workspace must be 256-byte aligned");
   hipStream_t s = as_stream(stream);
+  clear_stale_error();
   const PlanGeom geo = plan_geom(d);
   const PlanWs ws = plan_ws(d, workspace);
   const int P = d.S * d.K;

@@ -99,3 +99,15 @@ def test_binding_refuses_host_tensors():
     d = m.make_dims(2, 4, 1, 3, 1)
     with pytest.raises(ValueError, match="device tensor"):
         m.moonep_dispatch(d, 8, torch.zeros(6, 8), torch.zeros(6, dtype=torch.int32), torch.zeros(6, 8))
+
+
+def test_one_hip_runtime_in_process():
+    # the binding loads torch's HIP runtime before libmoonep.so, so only one libamdhip64 is mapped
+    import subprocess
+    import sys
+    code = ("import load_balanced_dispatch_amd, torch\n"
+            "libs = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}\n"
+            "print(len(libs))\n")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                         cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert out.stdout.strip().splitlines()[-1] == "1", out.stdout + out.stderr
