@@ -67,7 +67,13 @@ def histogram(topk_idx: np.ndarray, E: int) -> np.ndarray:
 
 
 def maxvio(counts: np.ndarray, n_pairs: int) -> float:
-    """max_e(T_e / Tbar) - 1 with Tbar = N / E, evaluated as (E * max T) / N - 1 in float64."""
+    """max_e(T_e / Tbar) - 1 with Tbar = N / E, evaluated as (E * max T) / N - 1 in float64.
+
+    With no pairs at all (N = 0) the ratio is 0/0; the reading used here is that an
+    empty routing has no imbalance, maxvio = 0.
+    """
+    if n_pairs == 0:
+        return 0.0
     E = len(counts)
     return float(E * int(np.max(counts))) / float(n_pairs) - 1.0
 

@@ -85,6 +85,10 @@ def test_maxvio_closed_forms(E, K):
     assert abs(planner.maxvio(counts, n) - (E / K - 1)) < 1e-12
 
 
+def test_maxvio_of_empty_routing_is_zero():
+    assert planner.maxvio(np.zeros(8, dtype=np.int64), 0) == 0.0
+
+
 def test_stable_order_brute_force():
     rng = np.random.default_rng(5)
     ids = rng.integers(0, 7, size=300)
