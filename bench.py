@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--forward-only", action="store_true")
+    ap.add_argument("--profile-pass", action="store_true",
+                    help="for counter runs: 1 warm-up + --steps steps of the whole path, then one plain 1 GiB "
+                         "device copy whose FETCH_SIZE/WRITE_SIZE calibrate the traffic counters; prints no JSON")
     return ap.parse_args()
 
 
@@ -170,16 +173,16 @@ def cpu_baseline(wl, seed, alpha, tokens_per_rank):
     idx, gates = router_output(sw.R, sw.S, sw.E, sw.K, seed, alpha=alpha, zipf_s=sw.zipf_s)
     rng = np.random.default_rng(seed)
     X = rng.standard_normal((sw.R, sw.S, sw.H))
+    if sw.Hp is not None:  # inputs are drawn before the clock starts: only oracle work is timed
+        W = rng.standard_normal((sw.E, sw.H, sw.Hp)) / np.sqrt(sw.H)
+        dY = rng.standard_normal((sw.N, sw.Hp))
     t0 = time.perf_counter()
     p = oplanner.plan(idx, sw.E, sw.B)
     Xp = olayer.dispatch(X, p.dest_idx)
     if sw.Hp is not None:
-        W = rng.standard_normal((sw.E, sw.H, sw.Hp)) / np.sqrt(sw.H)
-        t0 = time.perf_counter() - (time.perf_counter() - t0)  # weight drawing is not oracle work
         Ws = olayer.prefetch(W, p.slot_expert)
         Yp = olayer.group_gemm(Xp, W, Ws, p.cu_seqlens, sw.P)
         olayer.combine(Yp, p.dest_idx, gates)
-        dY = rng.standard_normal((sw.N, sw.Hp))
         dWh = np.zeros_like(W)
         dWs = np.zeros((sw.R, sw.B, sw.H, sw.Hp))
         olayer.wgrad(Xp, dY, p.cu_seqlens, sw.P, dWh, dWs)
@@ -230,6 +233,20 @@ def main():
 
     log(f"workload {wl.description}; building buffers")
     L = make_layer(wl, backward)
+    if args.profile_pass:
+        load_inputs(L, wl, args.seed, alpha_of(head_target))
+        for _ in range(1 + args.steps):
+            for _, f in stage_calls(L, backward):
+                f()
+        torch.cuda.synchronize()
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)  # a plain copy kernel moving 1 GiB in and 1 GiB out
+        torch.cuda.synchronize()
+        log("profile pass done: stages", [n for n, _ in stage_calls(L, backward)], "then a 1 GiB copy")
+        return
     results = {}
     points = [head_target] + ([t for t in sweep_targets if t != head_target] if not args.no_sweep else [])
     for tgt in points:
@@ -272,7 +289,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
-        cpu = cpu_baseline(wl, args.seed, h["alpha"], tokens_per_rank=max(1, min(wl.S, 128)))
+        cpu = cpu_baseline(wl, args.seed, h["alpha"], tokens_per_rank=max(1, min(wl.S, 640)))
 
     sweep = []
     for tgt in points:

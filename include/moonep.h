@@ -163,6 +163,9 @@ int moonep_group_gemm(moonep_dims d, int32_t H, int32_t Hp, moonep_dtype t, cons
 int moonep_combine(moonep_dims d, int32_t D, moonep_dtype t, const void* Yp, const int32_t* dest_idx,
                    const float* gates, float* out, moonep_stream stream);
 
+/* Bytes of device workspace moonep_wgrad needs. */
+size_t moonep_wgrad_workspace_bytes(moonep_dims d);
+
 /*
  * moonep_wgrad -- weight-gradient group GEMM into the float32 gradient
  * buffers ([P2] "Memory contract": an fp32 [E+B,H,Hp] gradient per projection
@@ -174,9 +177,12 @@ int moonep_combine(moonep_dims d, int32_t D, moonep_dtype t, const void* Yp, con
  *   dW_slots[r,j].  Groups with no rows leave their gradient untouched.
  * In:  Xp [R*S*K,H], dY [R*S*K,Hp] dtype t;  cu_seqlens [R,E+B+1].
  * In/Out: dW_home [E,H,Hp] float32;  dW_slots [R,B,H,Hp] float32 (NULL when B == 0).
+ * workspace: moonep_wgrad_workspace_bytes(d) bytes of device memory (256-byte aligned), contents
+ * ignored on entry (it holds the list of gradient jobs that have rows).
  */
 int moonep_wgrad(moonep_dims d, int32_t H, int32_t Hp, moonep_dtype t, const void* Xp, const void* dY,
-                 const int32_t* cu_seqlens, float* dW_home, float* dW_slots, moonep_stream stream);
+                 const int32_t* cu_seqlens, float* dW_home, float* dW_slots, void* workspace,
+                 moonep_stream stream);
 
 /*
  * moonep_reduce_grad -- fold redundant-expert gradients back to their home

@@ -8,7 +8,7 @@ no CPU or PyTorch fallback.
 """
 from ._lib import (  # noqa: F401
     Dims, MoonepError, LIB_PATH, SYMBOLS, MOONEP_F32, MOONEP_BF16, make_dims, last_error,
-    moonep_plan_workspace_bytes, moonep_group_gemm_workspace_bytes, moonep_plan, moonep_dispatch,
+    moonep_plan_workspace_bytes, moonep_group_gemm_workspace_bytes, moonep_wgrad_workspace_bytes, moonep_plan, moonep_dispatch,
     moonep_prefetch, moonep_group_gemm, moonep_combine, moonep_wgrad, moonep_reduce_grad,
 )
 from .layer import MoeLayer  # noqa: F401

@@ -50,7 +50,7 @@ def _load():
     # and two HIP runtimes in one process leave the library's launches without a device.
     import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m load_balanced_dispatch_amd.build`")
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python load_balanced_dispatch_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     sig = {
@@ -62,7 +62,8 @@ def _load():
         "moonep_group_gemm_workspace_bytes": (sz, [Dims]),
         "moonep_group_gemm": (ctypes.c_int, [Dims, i32, i32, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp]),
         "moonep_combine": (ctypes.c_int, [Dims, i32, ctypes.c_int, vp, vp, vp, vp, vp]),
-        "moonep_wgrad": (ctypes.c_int, [Dims, i32, i32, ctypes.c_int, vp, vp, vp, vp, vp, vp]),
+        "moonep_wgrad_workspace_bytes": (sz, [Dims]),
+        "moonep_wgrad": (ctypes.c_int, [Dims, i32, i32, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp]),
         "moonep_reduce_grad": (ctypes.c_int, [Dims, i32, i32, vp, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
@@ -76,8 +77,8 @@ _LIB = _load()
 
 # exported symbol names, as declared in include/moonep.h
 SYMBOLS = ("moonep_last_error", "moonep_plan_workspace_bytes", "moonep_plan", "moonep_dispatch", "moonep_prefetch",
-           "moonep_group_gemm_workspace_bytes", "moonep_group_gemm", "moonep_combine", "moonep_wgrad",
-           "moonep_reduce_grad")
+           "moonep_group_gemm_workspace_bytes", "moonep_group_gemm", "moonep_combine",
+           "moonep_wgrad_workspace_bytes", "moonep_wgrad", "moonep_reduce_grad")
 
 
 def lib():
@@ -143,6 +144,10 @@ def moonep_group_gemm_workspace_bytes(d: Dims) -> int:
     return int(_LIB.moonep_group_gemm_workspace_bytes(d))
 
 
+def moonep_wgrad_workspace_bytes(d: Dims) -> int:
+    return int(_LIB.moonep_wgrad_workspace_bytes(d))
+
+
 def moonep_plan(d: Dims, topk_idx, expert_counts, maxvio, cu_seqlens, slot_expert, dest_idx, src_of_row, stats,
                 workspace, stream=None):
     import torch
@@ -202,15 +207,17 @@ def moonep_combine(d: Dims, D: int, Yp, dest_idx, gates, out, stream=None):
                                _ptr(out, "out", torch.float32, d.R * d.S * D), _stream(stream)))
 
 
-def moonep_wgrad(d: Dims, H: int, Hp: int, Xp, dY, cu_seqlens, dW_home, dW_slots, stream=None):
+def moonep_wgrad(d: Dims, H: int, Hp: int, Xp, dY, cu_seqlens, dW_home, dW_slots, workspace, stream=None):
     import torch
     t = _dtype_enum(Xp)
+    if workspace.numel() * workspace.element_size() < moonep_wgrad_workspace_bytes(d):
+        raise ValueError("wgrad workspace too small")
     _check(_LIB.moonep_wgrad(d, int(H), int(Hp), t, _ptr(Xp, "Xp", Xp.dtype, d.N * H),
                              _ptr(dY, "dY", Xp.dtype, d.N * Hp),
                              _ptr(cu_seqlens, "cu_seqlens", torch.int32, d.R * (d.E + d.B + 1)),
                              _ptr(dW_home, "dW_home", torch.float32, d.E * H * Hp),
                              _ptr(dW_slots, "dW_slots", torch.float32, d.R * d.B * H * Hp, optional=d.B == 0),
-                             _stream(stream)))
+                             _ptr(workspace, "workspace"), _stream(stream)))
 
 
 def moonep_reduce_grad(d: Dims, H: int, Hp: int, slot_expert, dW_home, dW_slots, stream=None):

@@ -1,6 +1,8 @@
 """Builds libmoonep.so (all HIP sources under csrc/) for gfx950 with hipcc, in-tree.
 
-    python -m load_balanced_dispatch_amd.build [-v]
+    python load_balanced_dispatch_amd/build.py [-v]
+
+Run it as a file (not `-m`): importing the package loads the library it builds.
 """
 from __future__ import annotations
 

@@ -7,22 +7,16 @@
 // rank's prefetched slots.
 //
 // Design on gfx950:
-//   * ggemm_tiles (one block) turns cu_seqlens into a prefix of M-tiles per
+//   * ggemm_tiles (one block) turns cu_seqlens into a prefix of 256-row M-tiles per
 //     (rank, group), in device memory, so the GEMM needs no host sync.
-//   * ggemm_bf16<BN> is persistent: one 256-thread block per CU walks the
-//     (m-tile, n-tile) list; tile ids are remapped so the blocks of one XCD
-//     (workgroups are dealt to the 8 XCDs round-robin) take consecutive tiles,
-//     which share the same expert weights and token rows in that XCD's L2.
-//     Block tile 256 x 128 x 32, four waves of 128 x 64, MFMA 32x32x16 bf16,
-//     two blocks per CU so one block's global loads overlap the other's MFMAs.
-//     Tiles go global -> registers -> LDS (double-buffered); the activation
-//     operand is read with ds_read_b128 (k contiguous), the weight operand --
-//     whose k runs along LDS rows -- with ds_read_b64_tr_b16.  A wave skips
-//     MFMAs of 32-row strips past the end of its group.
-//   * ggemm_generic<T> is a plain LDS-tiled FMA kernel for float32 and for
-//     bf16 shapes the MFMA kernel does not tile (H % 64 or Hp % 128 != 0).
-//   The epilogue rounds each 32-row strip to bf16 in LDS and writes whole
-//   16-byte row chunks.
+//   * fwd::ggemm_bf16 is persistent (one 512-thread block per CU), 256 x 256 x 32 block tiles,
+//     eight waves of 128 x 64 with MFMA 32x32x16 bf16.  Operands stream global -> LDS with
+//     global_load_lds_dwordx4 into a 4-stage ring; the activation operand (k contiguous) is read
+//     with ds_read_b128, the weight operand (k along LDS rows, as the [H, H'] layout stores it)
+//     with ds_read_b64_tr_b16; both LDS layouts are XOR-swizzled against bank conflicts.  The
+//     epilogue rounds one 32-row strip at a time to bf16 in LDS and writes whole 16-byte chunks.
+//   * ggemm_generic<T> is a plain LDS-tiled FMA kernel for float32 and for bf16 shapes the MFMA
+//     kernel does not tile (H % 32 or H' % 64 != 0).
 #include "block_scan.h"
 #include "mfma_tile.h"
 #include "moonep_common.h"
@@ -99,152 +93,176 @@ __device__ __forceinline__ int find_group(const int32_t* tstart, int NG, int mt)
 
 // ------------------------------------------------------------------ bf16 MFMA kernel
 
-template <int BN, int BK>
-struct FwdCfg {
-  static constexpr int BM = kMfmaBM;
-  static constexpr int LDA = BK + 8;   // row pitch 16 mod 64 bytes: conflict-free ds_read_b128 over 16 rows
-  static constexpr int LDB = BN + 32;  // row pitch = 64 mod 256 bytes for the transpose reads
-  static constexpr int WN = BN / 2;
-  static constexpr int TM = 4;         // 128 rows per wave / 32
-  static constexpr int TN = WN / 32;
-  static constexpr int KK = BK / 16;   // MFMA k-steps per stage
-  static constexpr int A_CPR = BK / 8;  // 16-byte chunks per A row
-  static constexpr int B_CPR = BN / 8;  // 16-byte chunks per B row
-  static constexpr int A_VEC = BM * BK / 8 / 256;  // 16-byte vectors per thread per stage
-  static constexpr int B_VEC = BK * BN / 8 / 256;
-  static constexpr int A_ROWS = 256 / A_CPR;  // rows covered by one pass of the block
-  static constexpr int B_ROWS = 256 / B_CPR;
-  static constexpr int A_STAGE = BM * LDA;   // elements per A stage
-  static constexpr int B_STAGE = BK * LDB;
-  static constexpr int SP = WN + 8;          // epilogue staging pitch (elements)
-  static constexpr int LDS_ELEMS = 2 * (A_STAGE + B_STAGE);
-  static_assert(4 * 32 * SP <= LDS_ELEMS, "epilogue staging must fit in the stage buffers");
-};
+namespace fwd {
+constexpr int BM = 256, BN = 256, BK = 32, STAGES = 4, NWAVES = 8;
+constexpr int A_STAGE = BM * BK;  // 64-byte rows; 16-byte chunks XOR-swizzled by row
+constexpr int B_STAGE = BK * BN;  // 512-byte rows; 64-byte blocks XOR-swizzled by row
+constexpr int STAGE = A_STAGE + B_STAGE;
+constexpr int WN = 64, TM = 4, TN = 2, KK = BK / 16;
+constexpr int SP = WN + 8;  // epilogue staging pitch (elements)
+constexpr int LDS_ELEMS = STAGES * STAGE;
+static_assert(NWAVES * 32 * SP <= LDS_ELEMS, "epilogue staging must fit in the ring");
 
-// Two blocks per CU (about 60 KB of LDS and <= 256 registers each), so one
-// block's global-load wait overlaps the other's MFMAs.
-template <int BN, int BK>
-__global__ __launch_bounds__(256, 2) void ggemm_bf16(const uint16_t* __restrict__ Xp,
+// A stage (rows = tokens, 4 chunks of 8 k-values per row): the chunk order is permuted per row so
+// that the 16-byte operand reads of 16 consecutive rows, and of the two k-halves of 8 rows, hit
+// distinct LDS banks.
+__device__ __forceinline__ int a_swz(int row) { return (((row >> 2) & 1) << 1) | ((row >> 3) & 1); }
+__device__ __forceinline__ int a_off(int row, int c) { return row * BK + 8 * (c ^ a_swz(row)); }
+// B stage (rows = k, 256 output columns): the 64-byte blocks of row k are permuted by k % 4 so the
+// four rows a transpose read touches land in different banks.
+__device__ __forceinline__ int b_off(int k, int n) { return k * BN + ((((n >> 5) ^ (k & 3)) << 5) | (n & 31)); }
+
+// Persistent: one 512-thread block per CU; tile ids are remapped so the blocks of one XCD
+// (workgroups are dealt to the 8 XCDs round-robin) take consecutive tiles, which share token rows
+// and expert weights in that XCD's L2.  Block tile 256 x 256 x 32; eight waves of 128 x 64
+// (MFMA 32x32x16 bf16, two waves per SIMD).  Operand tiles stream global -> LDS with
+// global_load_lds_dwordx4 into a 4-stage ring, three stages ahead of the MFMAs, with no
+// register staging.  The last n-tile may be narrower than 256 (H' % 256 != 0): its missing
+// columns load a repeated valid column and their waves skip MFMAs and stores.
+__global__ __launch_bounds__(512, 1) void ggemm_bf16(const uint16_t* __restrict__ Xp,
                                                      const uint16_t* __restrict__ W_home,
                                                      const uint16_t* __restrict__ W_slots,
                                                      const int32_t* __restrict__ cu,
                                                      const int32_t* __restrict__ tstart, uint16_t* __restrict__ Yp,
                                                      int R, int E, int B, int P, int H, int Hp) {
-  using C = FwdCfg<BN, BK>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[LDS_ELEMS];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w >> 2, wn = w & 3;
   const int G = E + B, G1 = G + 1, NG = R * G;
-  const int NT = Hp / BN;
+  const int NT = (Hp + BN - 1) / BN;
   const int total = tstart[NG] * NT;
   const int nblk = gridDim.x;
   const int vb = (nblk % 8 == 0) ? (int)(blockIdx.x % 8) * (nblk / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
   const int KT = H / BK;
-  // this thread's slice of each stage: A row a_r + i*A_ROWS, chunk a_c; B row b_r + i*B_ROWS, chunk b_c
-  const int a_r = t / C::A_CPR, a_c = t % C::A_CPR;
-  const int b_r = t / C::B_CPR, b_c = t % C::B_CPR;
-  uint16_t* const a_st = lds + a_r * C::LDA + a_c * 8;                  // + buf*A_STAGE + i*A_ROWS*LDA
-  uint16_t* const b_st = lds + 2 * C::A_STAGE + b_r * C::LDB + b_c * 8;  // + buf*B_STAGE + i*B_ROWS*LDB
+  const int a_lr = lane >> 2, a_ls = lane & 3;   // A: one wave instruction fills 16 rows
+  const int b_lr = lane >> 5, b_ls = lane & 31;  // B: one wave instruction fills 2 rows
 
   for (int tile = vb; tile < total; tile += nblk) {
     const int mt = tile / NT, nt = tile % NT;
     const int grp = find_group(tstart, NG, mt);
     const int r = grp / G, g = grp % G;
     const int c0 = cu[(int64_t)r * G1 + g], c1 = cu[(int64_t)r * G1 + g + 1];
-    const int mo = (mt - tstart[grp]) * C::BM;
-    const int rows = min(C::BM, c1 - c0 - mo);
+    const int mo = (mt - tstart[grp]) * BM;
+    const int rows = min(BM, c1 - c0 - mo);
     const int64_t row0 = (int64_t)r * P + c0 + mo;
     const uint16_t* Wg = g < E ? W_home + (int64_t)g * H * Hp : W_slots + ((int64_t)r * B + (g - E)) * H * Hp;
     const int n0 = nt * BN;
-    const int strips = min(C::TM, max(0, (rows - wm * 128 + 31) / 32));  // valid 32-row strips of this wave
+    const int width = min(BN, Hp - n0);
+    const int strips = min(TM, max(0, (rows - wm * 128 + 31) / 32));  // valid 32-row strips of this wave
+    const bool wave_cols = wn * WN < width;
+    const bool full = strips == TM && wave_cols;
 
-    // global sources; rows past the group end repeat the last valid row (their results are dropped)
-    const uint16_t* a_base = Xp + row0 * H + a_c * 8;
-    int a_off[C::A_VEC];
+    // global sources of this wave's four DMA instructions per stage (2 for A, 2 for B)
+    const uint16_t* a_src[2];
 #pragma unroll
-    for (int i = 0; i < C::A_VEC; ++i) a_off[i] = min(a_r + i * C::A_ROWS, rows - 1) * H;
-    const uint16_t* b_src = Wg + (int64_t)b_r * Hp + n0 + b_c * 8;
-
-    u32x4 ra[C::A_VEC], rb[C::B_VEC];
-    auto gload = [&](int kt) {
-#pragma unroll
-      for (int i = 0; i < C::A_VEC; ++i) ra[i] = *reinterpret_cast<const u32x4*>(a_base + a_off[i] + kt * BK);
-#pragma unroll
-      for (int i = 0; i < C::B_VEC; ++i)
-        rb[i] = *reinterpret_cast<const u32x4*>(b_src + ((int64_t)kt * BK + i * C::B_ROWS) * Hp);
-    };
-    auto sstore = [&](int buf) {
-#pragma unroll
-      for (int i = 0; i < C::A_VEC; ++i)
-        *reinterpret_cast<u32x4*>(a_st + buf * C::A_STAGE + i * C::A_ROWS * C::LDA) = ra[i];
-#pragma unroll
-      for (int i = 0; i < C::B_VEC; ++i)
-        *reinterpret_cast<u32x4*>(b_st + buf * C::B_STAGE + i * C::B_ROWS * C::LDB) = rb[i];
-    };
-    auto frags = [&](int buf, int kk, bf16x8 (&a)[C::TM], bf16x8 (&b)[C::TN]) {
-      const uint16_t* As = lds + buf * C::A_STAGE;
-      const uint16_t* Bs = lds + 2 * C::A_STAGE + buf * C::B_STAGE;
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j) b[j] = operand_rows_k(Bs, C::LDB, kk * 16, wn * C::WN + j * 32, lane);
-#pragma unroll
-      for (int i = 0; i < C::TM; ++i) a[i] = operand_cols_k(As, C::LDA, wm * 128 + i * 32, kk * 16, lane);
-    };
-
-    f32x16 acc[C::TM][C::TN];
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j) acc[i][j] = (f32x16)(0.f);
-
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-      const int buf = kt & 1;
-      if (kt + 1 < KT) gload(kt + 1);
-#pragma unroll
-      for (int kk = 0; kk < C::KK; ++kk) {
-        bf16x8 a[C::TM], b[C::TN];
-        frags(buf, kk, a, b);
-#pragma unroll
-        for (int i = 0; i < C::TM; ++i)
-          if (i < strips)
-#pragma unroll
-            for (int j = 0; j < C::TN; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
-      }
-      if (kt + 1 < KT) sstore(buf ^ 1);
-      __syncthreads();
+    for (int i = 0; i < 2; ++i) {
+      const int row = (2 * w + i) * 16 + a_lr;  // rows past the group end repeat its last row
+      a_src[i] = Xp + (row0 + min(row, rows - 1)) * H + 8 * (a_ls ^ a_swz(row));
     }
+    const uint16_t* b_src[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int k = (2 * w + i) * 2 + b_lr;
+      const int q = (b_ls >> 2) ^ (k & 3);
+      b_src[i] = Wg + (int64_t)k * Hp + min(n0 + (q * 4 + (b_ls & 3)) * 8, Hp - 8);
+    }
+    auto issue = [&](int kt) {
+      uint16_t* st = lds + (kt % STAGES) * STAGE;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) dma16(a_src[i] + kt * BK, st + (2 * w + i) * 512);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) dma16(b_src[i] + (int64_t)kt * BK * Hp, st + A_STAGE + (2 * w + i) * 512);
+    };
 
-    // epilogue, one 32-row strip at a time: round to bf16 into this wave's LDS
-    // region (accumulator layout), then 16-byte stores of the valid rows.
-    uint16_t* stage = lds + w * 32 * C::SP;
+    f32x16 acc[TM][TN];
 #pragma unroll
-    for (int i = 0; i < C::TM; ++i) {
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = (f32x16)(0.f);
+
+    for (int st = 0; st < STAGES - 1 && st < KT; ++st) issue(st);
+    for (int kt = 0; kt < KT; ++kt) {
+      // this wave's loads of stage kt are done once at most the later stages' loads are pending
+      if (kt + 2 < KT) wait_vmcnt<8>();
+      else if (kt + 1 < KT) wait_vmcnt<4>();
+      else wait_vmcnt<0>();
+      lds_barrier();  // ... and every wave's, and every wave is done with the slot refilled next
+      if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1);
+      const uint16_t* As = lds + (kt % STAGES) * STAGE;
+      const uint16_t* Bs = As + A_STAGE;
+      auto frag = [&](int kk, bf16x8 (&a)[TM], bf16x8 (&b)[TN]) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int grp4 = lane >> 4, c = lane & 15;
+          const int n = wn * WN + j * 32 + 16 * (grp4 & 1) + 4 * (c & 3);
+          const int k = kk * 16 + 8 * (grp4 >> 1) + (c >> 2);
+          const bf16x4 lo = lds_tr4(Bs + b_off(k, n));
+          const bf16x4 hi = lds_tr4(Bs + b_off(k + 4, n));
+          b[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const int row = wm * 128 + i * 32 + (lane & 31);
+          a[i] = *reinterpret_cast<const bf16x8*>(As + a_off(row, kk * 2 + (lane >> 5)));
+        }
+      };
+      if (full) {  // operands of the next k-step are read while this one's MFMAs run
+        bf16x8 a[2][TM], b[2][TN];
+        frag(0, a[0], b[0]);
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          if (kk + 1 < KK) frag(kk + 1, a[(kk + 1) & 1], b[(kk + 1) & 1]);
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(a[kk & 1][i], b[kk & 1][j], acc[i][j]);
+        }
+      } else if (wave_cols) {  // the group's last tile: skip the strips past its end
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          bf16x8 a[TM], b[TN];
+          frag(kk, a, b);
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+            if (i < strips)
+#pragma unroll
+              for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+        }
+      }
+    }
+    lds_barrier();  // the ring is free: every wave has read its last stage
+
+    // epilogue, one 32-row strip at a time: round to bf16 into this wave's LDS region
+    // (accumulator layout), then 16-byte stores of whole row chunks of the valid rows.
+    uint16_t* stage = lds + w * 32 * SP;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
       __builtin_amdgcn_sched_barrier(0);
-      if (i < strips) {
+      const bool live = i < strips && wave_cols;
+      if (live) {
 #pragma unroll
-        for (int j = 0; j < C::TN; ++j)
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
           for (int v = 0; v < 16; ++v)
-            stage[acc_row(v, lane) * C::SP + j * 32 + (lane & 31)] = f32_to_bf16(acc[i][j][v]);
+            stage[acc_row(v, lane) * SP + j * 32 + (lane & 31)] = f32_to_bf16(acc[i][j][v]);
       }
       __syncthreads();
-      if (i < strips) {
-        constexpr int CPR = C::WN / 8;  // 16-byte chunks per staged row
+      if (live) {
+        constexpr int CPR = WN / 8;
 #pragma unroll
         for (int q = lane; q < 32 * CPR; q += 64) {
           const int rr = q / CPR, cc = q % CPR;
           const int row = wm * 128 + i * 32 + rr;
           if (row < rows)
-            *reinterpret_cast<u32x4*>(Yp + (row0 + row) * Hp + n0 + wn * C::WN + cc * 8) =
-                *reinterpret_cast<const u32x4*>(stage + rr * C::SP + cc * 8);
+            *reinterpret_cast<u32x4*>(Yp + (row0 + row) * Hp + n0 + wn * WN + cc * 8) =
+                *reinterpret_cast<const u32x4*>(stage + rr * SP + cc * 8);
         }
       }
       __syncthreads();
     }
   }
 }
+}  // namespace fwd
 
 // ------------------------------------------------------------------ generic kernel
 
@@ -351,7 +369,7 @@ extern "C" int moonep_group_gemm(moonep_dims d, int32_t H, int32_t Hp, moonep_dt
   hipLaunchKernelGGL(ggemm_tiles, dim3(1), dim3(1024), 0, s, cu_seqlens, d.R, d.E, d.B, t256, t64);
   MOONEP_LAUNCH_CHECK("moonep_group_gemm/tiles");
   const int cus = device_cu_count();
-  const bool mfma = t == MOONEP_BF16 && H % 32 == 0 && Hp % 128 == 0 && aligned16(Xp) &&
+  const bool mfma = t == MOONEP_BF16 && H % 32 == 0 && Hp % 64 == 0 && aligned16(Xp) &&
                     aligned16(W_home) && (d.B == 0 || aligned16(W_slots));
   if (mfma) {
     const auto* x = static_cast<const uint16_t*>(Xp);
@@ -359,8 +377,8 @@ extern "C" int moonep_group_gemm(moonep_dims d, int32_t H, int32_t Hp, moonep_dt
     const auto* ws = static_cast<const uint16_t*>(W_slots);
     auto* y = static_cast<uint16_t*>(Yp);
     const int P = d.S * d.K;
-    hipLaunchKernelGGL((ggemm_bf16<128, 32>), dim3(2 * cus), dim3(256), 0, s, x, wh, ws, cu_seqlens, t256, y, d.R,
-                       d.E, d.B, P, H, Hp);
+    hipLaunchKernelGGL(fwd::ggemm_bf16, dim3(cus), dim3(512), 0, s, x, wh, ws, cu_seqlens, t256, y, d.R, d.E, d.B,
+                       P, H, Hp);
   } else if (t == MOONEP_BF16) {
     hipLaunchKernelGGL(ggemm_generic<uint16_t>, dim3(cus * 4), dim3(256), 0, s, static_cast<const uint16_t*>(Xp),
                        static_cast<const uint16_t*>(W_home), static_cast<const uint16_t*>(W_slots), cu_seqlens, t64,

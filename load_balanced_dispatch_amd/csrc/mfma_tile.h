@@ -45,6 +45,27 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// 64 lanes x 16 bytes: lane l copies 16 bytes from its global address g to LDS at
+// lds_wave_base + 16*l (global_load_lds_dwordx4; lds_wave_base must be wave-uniform).  Issued
+// from asm so the compiler does not wait for every outstanding load before each LDS read: the
+// kernels wait on vmcnt themselves (wait_vmcnt) before a barrier.
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+__device__ __forceinline__ void dma16(const void* g, uint16_t* lds_wave_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_u16*)lds_wave_base);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
+}
+
+// Waits until at most N of this wave's vector-memory operations are outstanding (they retire in order).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier that does not drain outstanding loads (unlike __syncthreads, whose fence waits
+// for every memory operation); LDS visibility of the DMA'd stage is ensured by wait_vmcnt first.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Row of accumulator element v for lane l inside a 32x32 tile.
 __device__ __forceinline__ int acc_row(int v, int lane) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
 

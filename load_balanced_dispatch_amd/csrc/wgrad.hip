@@ -9,18 +9,18 @@
 // atomics: job e < E owns dW_home[e] and sums, in ascending rank order, the
 // rows every rank holds in its home-row group e (the home rank's kept rows and
 // other ranks' direct reads); job E + r*B + j owns slot j of rank r.  An output
-// tile is 256 (H) x 128 (H'), reduced over 32-row chunks of the job's rows with
-// MFMA 32x32x16 bf16.  Both operands reduce along LDS rows (token rows), so both
-// are read with ds_read_b64_tr_b16 from row-major tiles; rows past a segment
-// end are zero-filled.  A job without rows writes nothing.  The float32
-// read-modify-write of dW goes through LDS so it moves whole 16-byte row chunks.
+// tile is 256 (H) x 256 (H'), reduced over 32-row chunks of the job's rows with
+// MFMA 32x32x16 bf16 by eight waves; both operands reduce along token rows, so
+// both are read from LDS with ds_read_b64_tr_b16.  A job without rows writes
+// nothing.  The float32 read-modify-write of dW goes through LDS so it moves
+// whole 16-byte row chunks.
+#include "block_scan.h"
 #include "mfma_tile.h"
 #include "moonep_common.h"
 
 namespace moonep {
 namespace {
 
-constexpr int kWgBH = 256;
 constexpr int kGenBH = 64, kGenBN = 64, kGenBK = 16;
 
 // Walks the row segments of one job, ranks ascending, in chunks of `step` rows.
@@ -71,137 +71,178 @@ __device__ __forceinline__ SegWalk make_walk(const int32_t* cu, int job, int R, 
   return s;
 }
 
-template <int BN, int BK>
-struct WgCfg {
-  static constexpr int BH = kWgBH;
-  static constexpr int LDX = BH + 32;  // row pitch = 64 mod 256 bytes for the transpose reads
-  static constexpr int LDD = BN + 32;
-  static constexpr int WN = BN / 2;
-  static constexpr int TM = 4;  // 128 rows of dW per wave / 32
-  static constexpr int TN = WN / 32;
-  static constexpr int KK = BK / 16;
-  static constexpr int X_CPR = BH / 8, D_CPR = BN / 8;  // 16-byte chunks per staged row
-  static constexpr int X_VEC = BK * BH / 8 / 256;
-  static constexpr int D_VEC = BK * BN / 8 / 256;
-  static constexpr int X_ROWS = 256 / X_CPR, D_ROWS = 256 / D_CPR;
-  static constexpr int X_STAGE = BK * LDX, D_STAGE = BK * LDD;
-  static constexpr int LDS_ELEMS = 2 * (X_STAGE + D_STAGE);
-  static constexpr int SP = WN + 4;  // float32 epilogue staging pitch (floats)
-  static_assert(4 * 32 * SP * 2 <= LDS_ELEMS, "epilogue staging must fit in the stage buffers");
-};
+// Compacts the jobs that have rows (ascending job id) into jobs[0..n), n in jobs[J].
+__global__ __launch_bounds__(1024) void wgrad_jobs(const int32_t* __restrict__ cu, int R, int E, int B, int P,
+                                                  int32_t* __restrict__ jobs) {
+  __shared__ int32_t wsum[16];
+  const int J = E + R * B, G1 = E + B + 1;
+  auto has_rows = [&](int job) {
+    if (job < E) {
+      for (int r = 0; r < R; ++r)
+        if (cu[(int64_t)r * G1 + job + 1] > cu[(int64_t)r * G1 + job]) return true;
+      return false;
+    }
+    const int sj = job - E, r = sj / B, col = E + sj % B;
+    return cu[(int64_t)r * G1 + col + 1] > cu[(int64_t)r * G1 + col];
+  };
+  const int n = block_compact(J, has_rows, jobs, wsum);
+  if (threadIdx.x == 0) jobs[J] = n;
+}
 
-// Two blocks per CU (about 57 KB of LDS and <= 256 registers each).
-template <int BN, int BK>
-__global__ __launch_bounds__(256, 2) void wgrad_bf16(const uint16_t* __restrict__ Xp, const uint16_t* __restrict__ dY,
-                                                     const int32_t* __restrict__ cu, float* __restrict__ dW_home,
+namespace wg {
+constexpr int BH = 256, BN = 256, BK = 32, STAGES = 4, NWAVES = 8;
+constexpr int X_STAGE = BK * BH;  // 32 token rows x 256 h; 64-byte blocks XOR-swizzled by row
+constexpr int D_STAGE = BK * BN;  // 32 token rows x 256 n; same layout
+constexpr int STAGE = X_STAGE + D_STAGE;
+constexpr int WN = 64, TM = 4, TN = 2, KK = BK / 16;
+constexpr int SP = WN + 4;  // float32 epilogue staging pitch (floats)
+constexpr int LDS_ELEMS = STAGES * STAGE;
+static_assert(NWAVES * 32 * SP * 2 <= LDS_ELEMS, "epilogue staging must fit in the ring");
+
+__device__ __forceinline__ int blk_off(int k, int n) { return k * 256 + ((((n >> 5) ^ (k & 3)) << 5) | (n & 31)); }
+
+// One 512-byte row of zeros: rows past a segment's end load from here, so they add nothing.
+__device__ __attribute__((aligned(16))) uint16_t zero_row[256];
+
+__device__ __forceinline__ bf16x8 operand_rows(const uint16_t* T, int k0, int c0, int lane) {
+  const int grp = lane >> 4, c = lane & 15;
+  const int col = c0 + 16 * (grp & 1) + 4 * (c & 3);
+  const int row = k0 + 8 * (grp >> 1) + (c >> 2);
+  const bf16x4 lo = lds_tr4(T + blk_off(row, col));
+  const bf16x4 hi = lds_tr4(T + blk_off(row + 4, col));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Grid: 8 * ceil(J/8) job slots x (H/256) * ceil(H'/256) tiles, 512 threads.  Workgroups are dealt
+// to the 8 XCDs round-robin, so block b runs on XCD b % 8; XCD x takes the non-empty jobs
+// x, x+8, x+16, ... one after another, all tiles of a job at once (they share the job's rows in
+// that XCD's L2), and the empty tail lands last on every XCD.  Eight waves of 128 (h) x 64 (n);
+// both operands stream global -> LDS with global_load_lds_dwordx4 into a 4-stage ring of 32-row
+// chunks and are read with ds_read_b64_tr_b16 (the reduction runs along token rows).
+__global__ __launch_bounds__(512, 1) void wgrad_bf16(const uint16_t* __restrict__ Xp, const uint16_t* __restrict__ dY,
+                                                     const int32_t* __restrict__ cu,
+                                                     const int32_t* __restrict__ jobs, float* __restrict__ dW_home,
                                                      float* __restrict__ dW_slots, int R, int E, int B, int P, int H,
                                                      int Hp) {
-  using C = WgCfg<BN, BK>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[LDS_ELEMS];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int wm = w >> 1, wn = w & 1;
-  const int HT = H / C::BH, NT = Hp / BN;
+  const int wm = w >> 2, wn = w & 3;
+  const int HT = H / BH, NT = (Hp + BN - 1) / BN;
   const int per_job = HT * NT;
-  const int nblk = gridDim.x;
-  // XCD-aware: consecutive tiles of one job on one XCD share its rows in L2
-  const int bid = (nblk % 8 == 0) ? (int)(blockIdx.x % 8) * (nblk / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
-  const int job = bid / per_job, rem = bid % per_job;
-  const int ht = rem / NT, nt = rem % NT;
-  const int h0 = ht * C::BH, n0 = nt * BN;
+  const int xcd = blockIdx.x % 8, i_x = blockIdx.x / 8;
+  const int jj = (i_x / per_job) * 8 + xcd, rem = i_x % per_job;
+  if (jj >= jobs[E + R * B]) return;  // past the non-empty jobs
+  const int job = jobs[jj];
+  const int h0 = (rem / NT) * BH, n0 = (rem % NT) * BN;
+  const int width = min(BN, Hp - n0);
+  const bool wave_cols = wn * WN < width;
 
-  SegWalk walk = make_walk(cu, job, R, E, B, P);
-  if (!walk.seek(walk.r)) return;  // no rows: gradient untouched
+  // chunks of this job: 32-row pieces of each contributing rank's segment, ranks ascending
+  SegWalk count = make_walk(cu, job, R, E, B, P);
+  int nchunks = 0;
+  if (count.seek(count.r)) {
+    do ++nchunks; while (count.next(BK));
+  }
+  if (nchunks == 0) return;  // no rows: gradient untouched
   float* out = job < E ? dW_home + (int64_t)job * H * Hp : dW_slots + (int64_t)(job - E) * H * Hp;
 
-  const int x_r = t / C::X_CPR, x_c = t % C::X_CPR;
-  const int d_r = t / C::D_CPR, d_c = t % C::D_CPR;
-  const uint16_t* x_src = Xp + h0 + x_c * 8;
-  const uint16_t* d_src = dY + n0 + d_c * 8;
-  uint16_t* const x_st = lds + x_r * C::LDX + x_c * 8;
-  uint16_t* const d_st = lds + 2 * C::X_STAGE + d_r * C::LDD + d_c * 8;
-
-  u32x4 rx[C::X_VEC], rd[C::D_VEC];
-  auto gload = [&](int m, int end) {  // rows past the segment end load as zeros
+  // DMA slices: instruction j = 2w+i fills rows 2j, 2j+1 of the X stage, then of the D stage
+  const int r_l = lane >> 5, s_l = lane & 31;
+  int src_row[2], x_col[2], d_col[2];
 #pragma unroll
-    for (int i = 0; i < C::X_VEC; ++i) {
-      const int row = m + x_r + i * C::X_ROWS;
-      rx[i] = row < end ? *reinterpret_cast<const u32x4*>(x_src + (int64_t)row * H) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int i = 0; i < C::D_VEC; ++i) {
-      const int row = m + d_r + i * C::D_ROWS;
-      rd[i] = row < end ? *reinterpret_cast<const u32x4*>(d_src + (int64_t)row * Hp) : u32x4{0, 0, 0, 0};
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < C::X_VEC; ++i)
-      *reinterpret_cast<u32x4*>(x_st + buf * C::X_STAGE + i * C::X_ROWS * C::LDX) = rx[i];
-#pragma unroll
-    for (int i = 0; i < C::D_VEC; ++i)
-      *reinterpret_cast<u32x4*>(d_st + buf * C::D_STAGE + i * C::D_ROWS * C::LDD) = rd[i];
-  };
-
-  f32x16 acc[C::TM][C::TN];
-#pragma unroll
-  for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-    for (int j = 0; j < C::TN; ++j) acc[i][j] = (f32x16)(0.f);
-
-  gload(walk.m, walk.end);
-  sstore(0);
-  __syncthreads();
-  int buf = 0;
-  for (;;) {
-    const bool more = walk.next(BK);
-    if (more) gload(walk.m, walk.end);
-    const uint16_t* Xs = lds + buf * C::X_STAGE;
-    const uint16_t* Ds = lds + 2 * C::X_STAGE + buf * C::D_STAGE;
-#pragma unroll
-    for (int kk = 0; kk < C::KK; ++kk) {
-      bf16x8 a[C::TM], b[C::TN];
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j) b[j] = operand_rows_k(Ds, C::LDD, kk * 16, wn * C::WN + j * 32, lane);
-#pragma unroll
-      for (int i = 0; i < C::TM; ++i) a[i] = operand_rows_k(Xs, C::LDX, kk * 16, wm * 128 + i * 32, lane);
-#pragma unroll
-      for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
-    }
-    if (more) sstore(buf ^ 1);
-    __syncthreads();
-    if (!more) break;
-    buf ^= 1;
+  for (int i = 0; i < 2; ++i) {
+    src_row[i] = (2 * w + i) * 2 + r_l;
+    const int q = (s_l >> 2) ^ (src_row[i] & 3);
+    x_col[i] = (q * 4 + (s_l & 3)) * 8;
+    d_col[i] = x_col[i];
   }
+  SegWalk walk = make_walk(cu, job, R, E, B, P);
+  walk.seek(walk.r);
+  int issued = 0;
+  auto issue_next = [&]() {  // DMA of chunk `issued` into its ring slot, then advance the walker
+    uint16_t* st = lds + (issued % STAGES) * STAGE;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = walk.m + src_row[i];
+      const bool ok = row < walk.end;
+      const uint16_t* xs = ok ? Xp + (int64_t)row * H + h0 + x_col[i] : zero_row + x_col[i];
+      const int dc = min(n0 + d_col[i], Hp - 8);
+      const uint16_t* ds = ok ? dY + (int64_t)row * Hp + dc : zero_row + d_col[i];
+      dma16(xs, st + (2 * w + i) * 512);
+      dma16(ds, st + X_STAGE + (2 * w + i) * 512);
+    }
+    ++issued;
+    walk.next(BK);
+  };
 
-  // epilogue, one 32-row strip at a time: stage the float32 strip in this wave's
-  // LDS region, then dW += strip with 16-byte read-modify-writes of whole rows.
-  float* stage = reinterpret_cast<float*>(lds) + w * 32 * C::SP;
+  f32x16 acc[TM][TN];
 #pragma unroll
-  for (int i = 0; i < C::TM; ++i) {
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = (f32x16)(0.f);
+
+  for (int st = 0; st < STAGES - 1 && st < nchunks; ++st) issue_next();
+  for (int kt = 0; kt < nchunks; ++kt) {
+    if (kt + 2 < nchunks) wait_vmcnt<8>();
+    else if (kt + 1 < nchunks) wait_vmcnt<4>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    if (issued < nchunks) issue_next();
+    const uint16_t* Xs = lds + (kt % STAGES) * STAGE;
+    const uint16_t* Ds = Xs + X_STAGE;
+    if (wave_cols) {
+      bf16x8 a[2][TM], b[2][TN];
+      auto frag = [&](int kk, bf16x8 (&fa)[TM], bf16x8 (&fb)[TN]) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) fb[j] = operand_rows(Ds, kk * 16, wn * WN + j * 32, lane);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) fa[i] = operand_rows(Xs, kk * 16, wm * 128 + i * 32, lane);
+      };
+      frag(0, a[0], b[0]);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        if (kk + 1 < KK) frag(kk + 1, a[(kk + 1) & 1], b[(kk + 1) & 1]);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(a[kk & 1][i], b[kk & 1][j], acc[i][j]);
+      }
+    }
+  }
+  lds_barrier();
+
+  // epilogue, one 32-row strip at a time: stage the float32 strip in this wave's LDS region, then
+  // dW += strip with 16-byte read-modify-writes of whole row chunks
+  float* stage = reinterpret_cast<float*>(lds) + w * 32 * SP;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
     __builtin_amdgcn_sched_barrier(0);
+    if (wave_cols) {
 #pragma unroll
-    for (int j = 0; j < C::TN; ++j)
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) stage[acc_row(v, lane) * C::SP + j * 32 + (lane & 31)] = acc[i][j][v];
+        for (int v = 0; v < 16; ++v) stage[acc_row(v, lane) * SP + j * 32 + (lane & 31)] = acc[i][j][v];
+    }
     __syncthreads();
-    constexpr int CPR = C::WN / 4;  // 16-byte chunks per staged row
+    if (wave_cols) {
+      constexpr int CPR = WN / 4;
 #pragma unroll
-    for (int q = lane; q < 32 * CPR; q += 64) {
-      const int rr = q / CPR, cc = q % CPR;
-      f32x4* p = reinterpret_cast<f32x4*>(out + (int64_t)(h0 + wm * 128 + i * 32 + rr) * Hp + n0 + wn * C::WN + cc * 4);
-      const f32x4 s = *reinterpret_cast<const f32x4*>(stage + rr * C::SP + cc * 4);
-      f32x4 v = *p;
-      v[0] = v[0] + s[0];
-      v[1] = v[1] + s[1];
-      v[2] = v[2] + s[2];
-      v[3] = v[3] + s[3];
-      *p = v;
+      for (int q = lane; q < 32 * CPR; q += 64) {
+        const int rr = q / CPR, cc = q % CPR;
+        f32x4* p = reinterpret_cast<f32x4*>(out + (int64_t)(h0 + wm * 128 + i * 32 + rr) * Hp + n0 + wn * WN + cc * 4);
+        const f32x4 s = *reinterpret_cast<const f32x4*>(stage + rr * SP + cc * 4);
+        f32x4 v = *p;
+        v[0] = v[0] + s[0];
+        v[1] = v[1] + s[1];
+        v[2] = v[2] + s[2];
+        v[3] = v[3] + s[3];
+        *p = v;
+      }
     }
     __syncthreads();
   }
 }
+}  // namespace wg
 
 // ------------------------------------------------------------------ generic kernel
 
@@ -271,27 +312,37 @@ __global__ __launch_bounds__(256) void wgrad_generic(const T* __restrict__ Xp, c
 
 using namespace moonep;
 
+extern "C" size_t moonep_wgrad_workspace_bytes(moonep_dims d) {
+  if (check_dims(d, "moonep_wgrad_workspace_bytes") != MOONEP_OK) return 0;
+  return (((size_t)d.E + (size_t)d.R * d.B + 1) * sizeof(int32_t) + 255) & ~size_t(255);
+}
+
 extern "C" int moonep_wgrad(moonep_dims d, int32_t H, int32_t Hp, moonep_dtype t, const void* Xp, const void* dY,
-                            const int32_t* cu_seqlens, float* dW_home, float* dW_slots, moonep_stream stream) {
+                            const int32_t* cu_seqlens, float* dW_home, float* dW_slots, void* workspace,
+                            moonep_stream stream) {
   if (int rc = check_dims(d, "moonep_wgrad")) return rc;
   MOONEP_REQUIRE(t == MOONEP_F32 || t == MOONEP_BF16, "moonep_wgrad: bad dtype %d", (int)t);
   MOONEP_REQUIRE(H >= 1 && Hp >= 1, "moonep_wgrad: H and Hp must be >= 1");
   if (n_pairs(d) == 0) return MOONEP_OK;
-  MOONEP_REQUIRE(Xp && dY && cu_seqlens && dW_home, "moonep_wgrad: null pointer");
+  MOONEP_REQUIRE(Xp && dY && cu_seqlens && dW_home && workspace, "moonep_wgrad: null pointer");
   MOONEP_REQUIRE(d.B == 0 || dW_slots, "moonep_wgrad: dW_slots is null with B > 0");
+  MOONEP_REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, "moonep_wgrad: workspace must be 256-byte aligned");
   hipStream_t s = as_stream(stream);
   clear_stale_error();
   const int64_t jobs = (int64_t)d.E + (int64_t)d.R * d.B;
+  MOONEP_REQUIRE(jobs < (int64_t(1) << 28), "moonep_wgrad: too many jobs");
   const int P = d.S * d.K;
-  const bool mfma = t == MOONEP_BF16 && H % kWgBH == 0 && Hp % 128 == 0 && aligned16(Xp) && aligned16(dY) &&
+  const bool mfma = t == MOONEP_BF16 && H % wg::BH == 0 && Hp % 64 == 0 && aligned16(Xp) && aligned16(dY) &&
                     aligned16(dW_home) && (d.B == 0 || aligned16(dW_slots));
   if (mfma) {
-    const int BN = 128;
-    const int64_t blocks = jobs * (H / kWgBH) * (Hp / BN);
+    int32_t* job_list = static_cast<int32_t*>(workspace);
+    hipLaunchKernelGGL(wgrad_jobs, dim3(1), dim3(1024), 0, s, cu_seqlens, d.R, d.E, d.B, P, job_list);
+    MOONEP_LAUNCH_CHECK("moonep_wgrad/jobs");
+    const int64_t blocks = 8 * ((jobs + 7) / 8) * (H / wg::BH) * ((Hp + wg::BN - 1) / wg::BN);
     MOONEP_REQUIRE(blocks < (int64_t(1) << 31), "moonep_wgrad: grid too large");
     const auto* x = static_cast<const uint16_t*>(Xp);
     const auto* dy = static_cast<const uint16_t*>(dY);
-    hipLaunchKernelGGL((wgrad_bf16<128, 32>), dim3((unsigned)blocks), dim3(256), 0, s, x, dy, cu_seqlens, dW_home,
+    hipLaunchKernelGGL(wg::wgrad_bf16, dim3((unsigned)blocks), dim3(512), 0, s, x, dy, cu_seqlens, job_list, dW_home,
                        dW_slots, d.R, d.E, d.B, P, H, Hp);
   } else {
     const int64_t blocks = jobs * ((H + kGenBH - 1) / kGenBH) * ((Hp + kGenBN - 1) / kGenBN);

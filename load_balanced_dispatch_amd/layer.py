@@ -49,6 +49,8 @@ class MoeLayer:
                 self.dY = torch.zeros((N, Hp), dtype=dtype, device=device)
                 self.dW_home = torch.zeros((E, H, Hp), dtype=torch.float32, device=device)
                 self.dW_slots = torch.zeros((R, B, H, Hp), dtype=torch.float32, device=device)
+                self.ws_wgrad = torch.empty(max(1, _lib.moonep_wgrad_workspace_bytes(d)), dtype=torch.uint8,
+                                            device=device)
 
     # ---------------------------------------------------------------- steps
     def plan(self, stream=None):
@@ -72,7 +74,7 @@ class MoeLayer:
 
     def wgrad(self, stream=None):
         _lib.moonep_wgrad(self.d, self.H, self.Hp, self.Xp, self.dY, self.cu_seqlens, self.dW_home,
-                          self.dW_slots if self.d.B > 0 else None, stream)
+                          self.dW_slots if self.d.B > 0 else None, self.ws_wgrad, stream)
 
     def reduce_grad(self, stream=None):
         _lib.moonep_reduce_grad(self.d, self.H, self.Hp, self.slot_expert if self.d.B > 0 else None, self.dW_home,

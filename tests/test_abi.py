@@ -57,13 +57,14 @@ def test_bad_dims_rejected_everywhere(dims, msg):
         lambda: L.moonep_prefetch(d, 8, 8, 1, null, null, null, null),
         lambda: L.moonep_group_gemm(d, 8, 8, 1, *([null] * 7)),
         lambda: L.moonep_combine(d, 8, 1, null, null, null, null, null),
-        lambda: L.moonep_wgrad(d, 8, 8, 1, *([null] * 6)),
+        lambda: L.moonep_wgrad(d, 8, 8, 1, *([null] * 7)),
         lambda: L.moonep_reduce_grad(d, 8, 8, null, null, null, null),
     ]
     for c in calls:
         assert c() == _lib.MOONEP_EINVAL
         assert msg in m.last_error()
     assert m.moonep_plan_workspace_bytes(d) == 0
+    assert m.moonep_wgrad_workspace_bytes(d) == 0
 
 
 def test_null_pointers_rejected():
@@ -73,7 +74,7 @@ def test_null_pointers_rejected():
     assert "null" in m.last_error()
     assert L.moonep_dispatch(d, 8, 1, None, None, None, None) == _lib.MOONEP_EINVAL
     assert L.moonep_group_gemm(d, 8, 8, 1, *([None] * 7)) == _lib.MOONEP_EINVAL
-    assert L.moonep_wgrad(d, 8, 8, 1, *([None] * 6)) == _lib.MOONEP_EINVAL
+    assert L.moonep_wgrad(d, 8, 8, 1, *([None] * 7)) == _lib.MOONEP_EINVAL
     assert L.moonep_reduce_grad(d, 8, 8, None, None, None, None) == _lib.MOONEP_EINVAL
 
 
@@ -91,7 +92,7 @@ def test_empty_work_is_a_no_op():
     assert L.moonep_dispatch(d, 8, 1, None, None, None, None) == _lib.MOONEP_OK
     assert L.moonep_combine(d, 8, 1, None, None, None, None, None) == _lib.MOONEP_OK
     assert L.moonep_group_gemm(d, 8, 8, 1, *([None] * 7)) == _lib.MOONEP_OK
-    assert L.moonep_wgrad(d, 8, 8, 1, *([None] * 6)) == _lib.MOONEP_OK
+    assert L.moonep_wgrad(d, 8, 8, 1, *([None] * 7)) == _lib.MOONEP_OK
 
 
 def test_binding_refuses_host_tensors():
@@ -111,3 +112,15 @@ def test_one_hip_runtime_in_process():
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
                          cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
     assert out.stdout.strip().splitlines()[-1] == "1", out.stdout + out.stderr
+
+
+def test_build_script_loads_without_the_library():
+    # build() must work on a fresh checkout: its module is loaded by path, never through the package
+    import importlib.util
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    spec = importlib.util.spec_from_file_location("moonep_build_probe",
+                                                  os.path.join(root, "load_balanced_dispatch_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    assert callable(mod.build) and mod.ARCH == "gfx950"
+    assert "-packed-fp32-ops" in mod.FLAGS

@@ -285,7 +285,9 @@ def test_wgrad_accumulates(m, dtype, R, E, B, S, K, H, Hp):
     dWh = f32(init_h)
     dWs = f32(init_s) if B > 0 else None
     say("wgrad", dtype, R, E, B, S, K, H, Hp)
-    m.moonep_wgrad(m.make_dims(R, E, B, S, K), H, Hp, Xp, dY, i32(p.cu_seqlens), dWh, dWs)
+    d = m.make_dims(R, E, B, S, K)
+    ws = torch.full((m.moonep_wgrad_workspace_bytes(d),), 0xCD, dtype=torch.uint8, device=DEV)
+    m.moonep_wgrad(d, H, Hp, Xp, dY, i32(p.cu_seqlens), dWh, dWs, ws)
     torch.cuda.synchronize()
     rh, rs = init_h.copy(), init_s.copy()
     olayer.wgrad(np64(Xp), np64(dY), p.cu_seqlens, S * K, rh, rs)
