@@ -181,52 +181,72 @@ __global__ __launch_bounds__(512, 1) void ggemm_bf16(const uint16_t* __restrict_
       for (int j = 0; j < TN; ++j) acc[i][j] = (f32x16)(0.f);
 
     for (int st = 0; st < STAGES - 1 && st < KT; ++st) issue(st);
-    for (int kt = 0; kt < KT; ++kt) {
-      // this wave's loads of stage kt are done once at most the later stages' loads are pending
-      if (kt + 2 < KT) wait_vmcnt<8>();
-      else if (kt + 1 < KT) wait_vmcnt<4>();
-      else wait_vmcnt<0>();
-      lds_barrier();  // ... and every wave's, and every wave is done with the slot refilled next
-      if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1);
+    auto frag = [&](int kt, int kk, bf16x8 (&a)[TM], bf16x8 (&b)[TN]) {
       const uint16_t* As = lds + (kt % STAGES) * STAGE;
       const uint16_t* Bs = As + A_STAGE;
-      auto frag = [&](int kk, bf16x8 (&a)[TM], bf16x8 (&b)[TN]) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int grp4 = lane >> 4, c = lane & 15;
-          const int n = wn * WN + j * 32 + 16 * (grp4 & 1) + 4 * (c & 3);
-          const int k = kk * 16 + 8 * (grp4 >> 1) + (c >> 2);
-          const bf16x4 lo = lds_tr4(Bs + b_off(k, n));
-          const bf16x4 hi = lds_tr4(Bs + b_off(k + 4, n));
-          b[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      for (int j = 0; j < TN; ++j) {
+        const int grp4 = lane >> 4, c = lane & 15;
+        const int n = wn * WN + j * 32 + 16 * (grp4 & 1) + 4 * (c & 3);
+        const int k = kk * 16 + 8 * (grp4 >> 1) + (c >> 2);
+        const bf16x4 lo = lds_tr4(Bs + b_off(k, n));
+        const bf16x4 hi = lds_tr4(Bs + b_off(k + 4, n));
+        b[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int row = wm * 128 + i * 32 + (lane & 31);
+        a[i] = *reinterpret_cast<const bf16x8*>(As + a_off(row, kk * 2 + (lane >> 5)));
+      }
+    };
+    auto mma = [&](const bf16x8 (&a)[TM], const bf16x8 (&b)[TN]) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+    };
+    // stage 0 ready
+    if (KT > 2) wait_vmcnt<8>();
+    else if (KT > 1) wait_vmcnt<4>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    if (full) {
+      // the barrier sits between the two k-steps of a stage, so every LDS read overlaps MFMAs:
+      // reads of (kt, 1) run under the MFMAs of (kt, 0), reads of (kt+1, 0) under those of (kt, 1)
+      bf16x8 a0[TM], b0[TN], a1[TM], b1[TN];
+      frag(0, 0, a0, b0);
+      for (int kt = 0; kt < KT; ++kt) {
+        frag(kt, 1, a1, b1);
+        mma(a0, b0);
+        if (kt + 1 < KT) {
+          if (kt + 2 < KT) wait_vmcnt<4>();
+          else wait_vmcnt<0>();
+          lds_barrier();  // stage kt+1 landed everywhere; every wave is done with stage kt-1
+          if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1);
+          frag(kt + 1, 0, a0, b0);
         }
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          const int row = wm * 128 + i * 32 + (lane & 31);
-          a[i] = *reinterpret_cast<const bf16x8*>(As + a_off(row, kk * 2 + (lane >> 5)));
+        mma(a1, b1);
+      }
+    } else {
+      for (int kt = 0; kt < KT; ++kt) {
+        if (kt > 0) {  // stage kt landed everywhere; every wave is done with stage kt-1
+          if (kt + 2 < KT) wait_vmcnt<8>();
+          else if (kt + 1 < KT) wait_vmcnt<4>();
+          else wait_vmcnt<0>();
+          lds_barrier();
         }
-      };
-      if (full) {  // operands of the next k-step are read while this one's MFMAs run
-        bf16x8 a[2][TM], b[2][TN];
-        frag(0, a[0], b[0]);
+        if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1);
+        if (wave_cols) {
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          if (kk + 1 < KK) frag(kk + 1, a[(kk + 1) & 1], b[(kk + 1) & 1]);
+          for (int kk = 0; kk < KK; ++kk) {
+            bf16x8 a[TM], b[TN];
+            frag(kt, kk, a, b);
 #pragma unroll
-          for (int i = 0; i < TM; ++i)
+            for (int i = 0; i < TM; ++i)
+              if (i < strips)
 #pragma unroll
-            for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(a[kk & 1][i], b[kk & 1][j], acc[i][j]);
-        }
-      } else if (wave_cols) {  // the group's last tile: skip the strips past its end
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          bf16x8 a[TM], b[TN];
-          frag(kk, a, b);
-#pragma unroll
-          for (int i = 0; i < TM; ++i)
-            if (i < strips)
-#pragma unroll
-              for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+                for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+          }
         }
       }
     }

@@ -71,22 +71,79 @@ __device__ __forceinline__ SegWalk make_walk(const int32_t* cu, int job, int R, 
   return s;
 }
 
-// Compacts the jobs that have rows (ascending job id) into jobs[0..n), n in jobs[J].
-__global__ __launch_bounds__(1024) void wgrad_jobs(const int32_t* __restrict__ cu, int R, int E, int B, int P,
-                                                  int32_t* __restrict__ jobs) {
+// Work list of the MFMA kernel, in the workspace (int32 words; J = E + R*B jobs):
+//   [0]                       n, the number of jobs that have rows
+//   [32 * (1 + x)]            next unclaimed unit of queue x, x = 0..7 (one 128-byte line each)
+//   [kSchedHdr + p]           job at position p of the size order (p < n)
+//   [kSchedHdr + J + p]       its number of 32-row chunks
+//   [kSchedHdr + 2J + job]    chunk count of every job (scratch)
+constexpr int kQueues = 8, kSchedHdr = 32 * (1 + kQueues), kBuckets = 512;
+
+// 32-row chunks of a job: each contributing rank's segment rounded up, as the kernel walks them.
+__device__ __forceinline__ int job_chunks(const int32_t* cu, int job, int R, int E, int B) {
+  const int G1 = E + B + 1;
+  if (job < E) {
+    int c = 0;
+    for (int r = 0; r < R; ++r) c += (max(0, cu[(int64_t)r * G1 + job + 1] - cu[(int64_t)r * G1 + job]) + 31) >> 5;
+    return c;
+  }
+  const int sj = job - E, r = sj / B, col = E + sj % B;
+  return (max(0, cu[(int64_t)r * G1 + col + 1] - cu[(int64_t)r * G1 + col]) + 31) >> 5;
+}
+
+// Size class of a job with c >= 1 chunks: 16 classes per octave (the float's exponent and top four
+// mantissa bits), numbered so that larger jobs get smaller classes; always in [0, kBuckets).
+__device__ __forceinline__ int size_class(int c) {
+  return kBuckets - 1 - ((int)(__float_as_uint((float)c) >> 19) - (127 << 4));
+}
+
+// One block of 1024: orders the jobs that have rows by size class, larger first, ties by job id
+// (a stable counting sort, so the order is deterministic), and clears the queue counters.
+__global__ __launch_bounds__(1024) void wgrad_schedule(const int32_t* __restrict__ cu, int R, int E, int B,
+                                                       int32_t* __restrict__ ws) {
+  __shared__ int32_t off[kBuckets];
   __shared__ int32_t wsum[16];
-  const int J = E + R * B, G1 = E + B + 1;
-  auto has_rows = [&](int job) {
-    if (job < E) {
-      for (int r = 0; r < R; ++r)
-        if (cu[(int64_t)r * G1 + job + 1] > cu[(int64_t)r * G1 + job]) return true;
-      return false;
+  const int J = E + R * B, t = threadIdx.x, w = t >> 6, nw = blockDim.x >> 6;
+  int32_t* sorted_job = ws + kSchedHdr;
+  int32_t* sorted_chunks = sorted_job + J;
+  int32_t* chunks = sorted_chunks + J;
+  for (int i = t; i < kBuckets; i += blockDim.x) off[i] = 0;
+  __syncthreads();
+  for (int j = t; j < J; j += blockDim.x) {  // thread t handles jobs t, t + 1024, ... in both passes
+    const int c = job_chunks(cu, j, R, E, B);
+    chunks[j] = c;
+    if (c > 0) atomicAdd(&off[size_class(c)], 1);
+  }
+  __syncthreads();
+  const int n = block_excl_scan(off, kBuckets, wsum);
+  for (int i0 = 0; i0 < J; i0 += blockDim.x) {
+    const int j = i0 + t;
+    const int c = j < J ? chunks[j] : 0;
+    const int b = c > 0 ? size_class(c) : -1;
+    // rank among the lanes of this wave in the same class, and the size of that group
+    int before = 0, group = 0;
+    uint64_t todo = __ballot(b >= 0);
+    while (todo) {
+      const int bl = __shfl(b, __builtin_ctzll(todo), 64);
+      const uint64_t m = __ballot(b == bl);
+      if (b == bl) {
+        before = __popcll(m & lanemask_lt());
+        group = __popcll(m);
+      }
+      todo &= ~m;
     }
-    const int sj = job - E, r = sj / B, col = E + sj % B;
-    return cu[(int64_t)r * G1 + col + 1] > cu[(int64_t)r * G1 + col];
-  };
-  const int n = block_compact(J, has_rows, jobs, wsum);
-  if (threadIdx.x == 0) jobs[J] = n;
+    for (int ww = 0; ww < nw; ++ww) {  // waves in order keep equal classes in job order
+      if (w == ww && b >= 0) {
+        const int pos = off[b] + before;
+        sorted_job[pos] = j;
+        sorted_chunks[pos] = c;
+        if (before == 0) off[b] = pos + group;
+      }
+      __syncthreads();
+    }
+  }
+  if (t == 0) ws[0] = n;
+  if (t < kQueues) ws[32 * (1 + t)] = 0;
 }
 
 namespace wg {
@@ -113,133 +170,155 @@ __device__ __forceinline__ bf16x8 operand_rows(const uint16_t* T, int k0, int c0
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// Grid: 8 * ceil(J/8) job slots x (H/256) * ceil(H'/256) tiles, 512 threads.  Workgroups are dealt
-// to the 8 XCDs round-robin, so block b runs on XCD b % 8; XCD x takes the non-empty jobs
-// x, x+8, x+16, ... one after another, all tiles of a job at once (they share the job's rows in
-// that XCD's L2), and the empty tail lands last on every XCD.  Eight waves of 128 (h) x 64 (n);
-// both operands stream global -> LDS with global_load_lds_dwordx4 into a 4-stage ring of 32-row
-// chunks and are read with ds_read_b64_tr_b16 (the reduction runs along token rows).
+// Persistent: one block of 512 per CU.  A unit is one output tile of one job; the jobs, larger
+// first, are dealt to 8 queues in snake order (queue slot q of queue x holds sorted position
+// 8q + x for even q, 8q + 7 - x for odd q) and a job's tiles follow one another in its queue.
+// Block b drains queue b % 8 first -- workgroups are dealt to the 8 XCDs round-robin, so that is
+// its own XCD's queue and a job's tiles share its rows in one L2 -- then takes what is left in
+// the other queues.  Units are claimed with an atomic counter per queue, so every unit runs
+// exactly once and every block stops once all 8 queues are empty.  Eight waves of 128 (h) x 64
+// (n); both operands stream global -> LDS with global_load_lds_dwordx4 into a 4-stage ring of
+// 32-row chunks and are read with ds_read_b64_tr_b16 (the reduction runs along token rows).
 __global__ __launch_bounds__(512, 1) void wgrad_bf16(const uint16_t* __restrict__ Xp, const uint16_t* __restrict__ dY,
-                                                     const int32_t* __restrict__ cu,
-                                                     const int32_t* __restrict__ jobs, float* __restrict__ dW_home,
-                                                     float* __restrict__ dW_slots, int R, int E, int B, int P, int H,
-                                                     int Hp) {
+                                                     const int32_t* __restrict__ cu, int32_t* ws,
+                                                     float* __restrict__ dW_home, float* __restrict__ dW_slots, int R,
+                                                     int E, int B, int P, int H, int Hp) {
   __shared__ __attribute__((aligned(1024))) uint16_t lds[LDS_ELEMS];
+  __shared__ int32_t s_unit[2];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int wm = w >> 2, wn = w & 3;
   const int HT = H / BH, NT = (Hp + BN - 1) / BN;
   const int per_job = HT * NT;
-  const int xcd = blockIdx.x % 8, i_x = blockIdx.x / 8;
-  const int jj = (i_x / per_job) * 8 + xcd, rem = i_x % per_job;
-  if (jj >= jobs[E + R * B]) return;  // past the non-empty jobs
-  const int job = jobs[jj];
-  const int h0 = (rem / NT) * BH, n0 = (rem % NT) * BN;
-  const int width = min(BN, Hp - n0);
-  const bool wave_cols = wn * WN < width;
+  const int J = E + R * B;
+  const int n = ws[0];
+  const int32_t* sorted_job = ws + kSchedHdr;
+  const int32_t* sorted_chunks = sorted_job + J;
+  const int home_q = blockIdx.x % kQueues;
+  int qd = 0;  // thread 0: queues home_q .. home_q + qd - 1 (mod 8) are known to be empty
 
-  // chunks of this job: 32-row pieces of each contributing rank's segment, ranks ascending
-  SegWalk count = make_walk(cu, job, R, E, B, P);
-  int nchunks = 0;
-  if (count.seek(count.r)) {
-    do ++nchunks; while (count.next(BK));
-  }
-  if (nchunks == 0) return;  // no rows: gradient untouched
-  float* out = job < E ? dW_home + (int64_t)job * H * Hp : dW_slots + (int64_t)(job - E) * H * Hp;
+  for (;;) {
+    if (t == 0) {
+      int pos = -1, tile = 0;
+      for (; qd < kQueues; ++qd) {
+        const int x = (home_q + qd) % kQueues;
+        const int u = atomicAdd(ws + 32 * (1 + x), 1);
+        const int q = u / per_job;
+        const int pp = 8 * q + ((q & 1) ? kQueues - 1 - x : x);
+        if (pp < n) {  // positions grow with u, so a queue that once came up empty stays empty
+          pos = pp;
+          tile = u % per_job;
+          break;
+        }
+      }
+      s_unit[0] = pos;
+      s_unit[1] = tile;
+    }
+    __syncthreads();
+    const int pos = s_unit[0], tile = s_unit[1];
+    __syncthreads();  // every wave holds the unit before thread 0 may claim the next one
+    if (pos < 0) break;
+    const int job = sorted_job[pos];
+    const int nchunks = sorted_chunks[pos];
+    const int h0 = (tile / NT) * BH, n0 = (tile % NT) * BN;
+    const int width = min(BN, Hp - n0);
+    const bool wave_cols = wn * WN < width;
+    float* out = job < E ? dW_home + (int64_t)job * H * Hp : dW_slots + (int64_t)(job - E) * H * Hp;
 
-  // DMA slices: instruction j = 2w+i fills rows 2j, 2j+1 of the X stage, then of the D stage
-  const int r_l = lane >> 5, s_l = lane & 31;
-  int src_row[2], x_col[2], d_col[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    src_row[i] = (2 * w + i) * 2 + r_l;
-    const int q = (s_l >> 2) ^ (src_row[i] & 3);
-    x_col[i] = (q * 4 + (s_l & 3)) * 8;
-    d_col[i] = x_col[i];
-  }
-  SegWalk walk = make_walk(cu, job, R, E, B, P);
-  walk.seek(walk.r);
-  int issued = 0;
-  auto issue_next = [&]() {  // DMA of chunk `issued` into its ring slot, then advance the walker
-    uint16_t* st = lds + (issued % STAGES) * STAGE;
+    // DMA slices: instruction j = 2w+i fills rows 2j, 2j+1 of the X stage, then of the D stage
+    const int r_l = lane >> 5, s_l = lane & 31;
+    int src_row[2], x_col[2], d_col[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int row = walk.m + src_row[i];
-      const bool ok = row < walk.end;
-      const uint16_t* xs = ok ? Xp + (int64_t)row * H + h0 + x_col[i] : zero_row + x_col[i];
-      const int dc = min(n0 + d_col[i], Hp - 8);
-      const uint16_t* ds = ok ? dY + (int64_t)row * Hp + dc : zero_row + d_col[i];
-      dma16(xs, st + (2 * w + i) * 512);
-      dma16(ds, st + X_STAGE + (2 * w + i) * 512);
+      src_row[i] = (2 * w + i) * 2 + r_l;
+      const int q = (s_l >> 2) ^ (src_row[i] & 3);
+      x_col[i] = (q * 4 + (s_l & 3)) * 8;
+      d_col[i] = x_col[i];
     }
-    ++issued;
-    walk.next(BK);
-  };
-
-  f32x16 acc[TM][TN];
+    SegWalk walk = make_walk(cu, job, R, E, B, P);
+    walk.seek(walk.r);
+    int issued = 0;
+    auto issue_next = [&]() {  // DMA of chunk `issued` into its ring slot, then advance the walker
+      uint16_t* st = lds + (issued % STAGES) * STAGE;
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = (f32x16)(0.f);
+      for (int i = 0; i < 2; ++i) {
+        const int row = walk.m + src_row[i];
+        const bool ok = row < walk.end;
+        const uint16_t* xs = ok ? Xp + (int64_t)row * H + h0 + x_col[i] : zero_row + x_col[i];
+        const int dc = min(n0 + d_col[i], Hp - 8);
+        const uint16_t* ds = ok ? dY + (int64_t)row * Hp + dc : zero_row + d_col[i];
+        dma16(xs, st + (2 * w + i) * 512);
+        dma16(ds, st + X_STAGE + (2 * w + i) * 512);
+      }
+      ++issued;
+      walk.next(BK);
+    };
 
-  for (int st = 0; st < STAGES - 1 && st < nchunks; ++st) issue_next();
-  for (int kt = 0; kt < nchunks; ++kt) {
-    if (kt + 2 < nchunks) wait_vmcnt<8>();
-    else if (kt + 1 < nchunks) wait_vmcnt<4>();
-    else wait_vmcnt<0>();
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = (f32x16)(0.f);
+
+    for (int st = 0; st < STAGES - 1 && st < nchunks; ++st) issue_next();
+    for (int kt = 0; kt < nchunks; ++kt) {
+      if (kt + 2 < nchunks) wait_vmcnt<8>();
+      else if (kt + 1 < nchunks) wait_vmcnt<4>();
+      else wait_vmcnt<0>();
+      lds_barrier();
+      if (issued < nchunks) issue_next();
+      const uint16_t* Xs = lds + (kt % STAGES) * STAGE;
+      const uint16_t* Ds = Xs + X_STAGE;
+      if (wave_cols) {
+        bf16x8 a[2][TM], b[2][TN];
+        auto frag = [&](int kk, bf16x8 (&fa)[TM], bf16x8 (&fb)[TN]) {
+#pragma unroll
+          for (int j = 0; j < TN; ++j) fb[j] = operand_rows(Ds, kk * 16, wn * WN + j * 32, lane);
+#pragma unroll
+          for (int i = 0; i < TM; ++i) fa[i] = operand_rows(Xs, kk * 16, wm * 128 + i * 32, lane);
+        };
+        frag(0, a[0], b[0]);
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          if (kk + 1 < KK) frag(kk + 1, a[(kk + 1) & 1], b[(kk + 1) & 1]);
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(a[kk & 1][i], b[kk & 1][j], acc[i][j]);
+        }
+      }
+    }
     lds_barrier();
-    if (issued < nchunks) issue_next();
-    const uint16_t* Xs = lds + (kt % STAGES) * STAGE;
-    const uint16_t* Ds = Xs + X_STAGE;
-    if (wave_cols) {
-      bf16x8 a[2][TM], b[2][TN];
-      auto frag = [&](int kk, bf16x8 (&fa)[TM], bf16x8 (&fb)[TN]) {
-#pragma unroll
-        for (int j = 0; j < TN; ++j) fb[j] = operand_rows(Ds, kk * 16, wn * WN + j * 32, lane);
-#pragma unroll
-        for (int i = 0; i < TM; ++i) fa[i] = operand_rows(Xs, kk * 16, wm * 128 + i * 32, lane);
-      };
-      frag(0, a[0], b[0]);
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        if (kk + 1 < KK) frag(kk + 1, a[(kk + 1) & 1], b[(kk + 1) & 1]);
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(a[kk & 1][i], b[kk & 1][j], acc[i][j]);
-      }
-    }
-  }
-  lds_barrier();
 
-  // epilogue, one 32-row strip at a time: stage the float32 strip in this wave's LDS region, then
-  // dW += strip with 16-byte read-modify-writes of whole row chunks
-  float* stage = reinterpret_cast<float*>(lds) + w * 32 * SP;
+    // epilogue, one 32-row strip at a time: stage the float32 strip in this wave's LDS region, then
+    // dW += strip with 16-byte read-modify-writes of whole row chunks
+    float* stage = reinterpret_cast<float*>(lds) + w * 32 * SP;
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    __builtin_amdgcn_sched_barrier(0);
-    if (wave_cols) {
+    for (int i = 0; i < TM; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (wave_cols) {
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) stage[acc_row(v, lane) * SP + j * 32 + (lane & 31)] = acc[i][j][v];
-    }
-    __syncthreads();
-    if (wave_cols) {
-      constexpr int CPR = WN / 4;
-#pragma unroll
-      for (int q = lane; q < 32 * CPR; q += 64) {
-        const int rr = q / CPR, cc = q % CPR;
-        f32x4* p = reinterpret_cast<f32x4*>(out + (int64_t)(h0 + wm * 128 + i * 32 + rr) * Hp + n0 + wn * WN + cc * 4);
-        const f32x4 s = *reinterpret_cast<const f32x4*>(stage + rr * SP + cc * 4);
-        f32x4 v = *p;
-        v[0] = v[0] + s[0];
-        v[1] = v[1] + s[1];
-        v[2] = v[2] + s[2];
-        v[3] = v[3] + s[3];
-        *p = v;
+          for (int v = 0; v < 16; ++v) stage[acc_row(v, lane) * SP + j * 32 + (lane & 31)] = acc[i][j][v];
       }
+      __syncthreads();
+      if (wave_cols) {
+        constexpr int CPR = WN / 4;
+#pragma unroll
+        for (int q = lane; q < 32 * CPR; q += 64) {
+          const int rr = q / CPR, cc = q % CPR;
+          f32x4* p = reinterpret_cast<f32x4*>(out + (int64_t)(h0 + wm * 128 + i * 32 + rr) * Hp + n0 + wn * WN + cc * 4);
+          const f32x4 s = *reinterpret_cast<const f32x4*>(stage + rr * SP + cc * 4);
+          f32x4 v = *p;
+          v[0] = v[0] + s[0];
+          v[1] = v[1] + s[1];
+          v[2] = v[2] + s[2];
+          v[3] = v[3] + s[3];
+          *p = v;
+        }
+      }
+      __syncthreads();
     }
-    __syncthreads();
   }
 }
 }  // namespace wg
@@ -314,7 +393,8 @@ using namespace moonep;
 
 extern "C" size_t moonep_wgrad_workspace_bytes(moonep_dims d) {
   if (check_dims(d, "moonep_wgrad_workspace_bytes") != MOONEP_OK) return 0;
-  return (((size_t)d.E + (size_t)d.R * d.B + 1) * sizeof(int32_t) + 255) & ~size_t(255);
+  const size_t jobs = (size_t)d.E + (size_t)d.R * d.B;
+  return (((size_t)kSchedHdr + 3 * jobs) * sizeof(int32_t) + 255) & ~size_t(255);
 }
 
 extern "C" int moonep_wgrad(moonep_dims d, int32_t H, int32_t Hp, moonep_dtype t, const void* Xp, const void* dY,
@@ -335,15 +415,16 @@ extern "C" int moonep_wgrad(moonep_dims d, int32_t H, int32_t Hp, moonep_dtype t
   const bool mfma = t == MOONEP_BF16 && H % wg::BH == 0 && Hp % 64 == 0 && aligned16(Xp) && aligned16(dY) &&
                     aligned16(dW_home) && (d.B == 0 || aligned16(dW_slots));
   if (mfma) {
-    int32_t* job_list = static_cast<int32_t*>(workspace);
-    hipLaunchKernelGGL(wgrad_jobs, dim3(1), dim3(1024), 0, s, cu_seqlens, d.R, d.E, d.B, P, job_list);
-    MOONEP_LAUNCH_CHECK("moonep_wgrad/jobs");
-    const int64_t blocks = 8 * ((jobs + 7) / 8) * (H / wg::BH) * ((Hp + wg::BN - 1) / wg::BN);
-    MOONEP_REQUIRE(blocks < (int64_t(1) << 31), "moonep_wgrad: grid too large");
+    const int cus = device_cu_count();
+    const int64_t units = jobs * (H / wg::BH) * ((Hp + wg::BN - 1) / wg::BN);
+    MOONEP_REQUIRE(units + 8 * (int64_t)cus < (int64_t(1) << 30), "moonep_wgrad: too many output tiles");
+    int32_t* ws = static_cast<int32_t*>(workspace);
+    hipLaunchKernelGGL(wgrad_schedule, dim3(1), dim3(1024), 0, s, cu_seqlens, d.R, d.E, d.B, ws);
+    MOONEP_LAUNCH_CHECK("moonep_wgrad/schedule");
     const auto* x = static_cast<const uint16_t*>(Xp);
     const auto* dy = static_cast<const uint16_t*>(dY);
-    hipLaunchKernelGGL(wg::wgrad_bf16, dim3((unsigned)blocks), dim3(512), 0, s, x, dy, cu_seqlens, job_list, dW_home,
-                       dW_slots, d.R, d.E, d.B, P, H, Hp);
+    hipLaunchKernelGGL(wg::wgrad_bf16, dim3((unsigned)cus), dim3(512), 0, s, x, dy, cu_seqlens, ws,
+                       dW_home, dW_slots, d.R, d.E, d.B, P, H, Hp);
   } else {
     const int64_t blocks = jobs * ((H + kGenBH - 1) / kGenBH) * ((Hp + kGenBN - 1) / kGenBN);
     MOONEP_REQUIRE(blocks < (int64_t(1) << 31), "moonep_wgrad: grid too large");
