@@ -17,8 +17,12 @@ a bounded sample.
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -27,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+MFMA_F32_VECTOR_TFLOPS = 157.3  # MI355X fp32 vector
 
 WORKLOAD_KEYS = {"tiny": "tiny_f32", "mid": "mid_fwd", "large": "large_fwd", "stress": "plan_stress"}
 
@@ -42,6 +47,11 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--forward-only", action="store_true")
+    ap.add_argument("--stats-md", metavar="CSV",
+                    help="print a markdown table of the library kernels in a rocprofv3 kernel_stats.csv; no GPU")
+    ap.add_argument("--traffic-md", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="print the per-stage HBM traffic summary of two --profile-pass counter runs "
+                         "(FETCH_SIZE, WRITE_SIZE) for --workload/--maxvio; no GPU")
     ap.add_argument("--profile-pass", action="store_true",
                     help="for counter runs: 1 warm-up + --steps steps of the whole path, then one plain 1 GiB "
                          "device copy whose FETCH_SIZE/WRITE_SIZE calibrate the traffic counters; prints no JSON")
@@ -93,72 +103,192 @@ def stage_calls(L, backward):
 
 
 def time_steps(L, backward, steps, warmup):
-    """Headline timing: K whole steps between two device synchronisations, with HIP events around the
-    dominant kernel's call on the same (current) stream."""
+    """K whole steps between two device synchronisations (wall clock), with HIP events recorded between
+    consecutive calls on the stream the kernels run on (torch's current stream), so every stage's average
+    launch duration comes from the same timed region."""
     import torch
     calls = stage_calls(L, backward)
     for _ in range(warmup):
         for _, f in calls:
             f()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(steps):
-        for name, f in calls:
-            if name == "group_gemm":
-                ev[s][0].record()
-                f()
-                ev[s][1].record()
-            else:
-                f()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    gemm_ms = [a.elapsed_time(b) for a, b in ev] if L.Hp is not None else []
-    return (t1 - t0) * 1e3 / steps, (sum(gemm_ms) / len(gemm_ms) if gemm_ms else None)
-
-
-def time_stages(L, backward, reps=10):
-    """Per-stage breakdown: events between consecutive calls of each step, averaged."""
-    import torch
-    calls = stage_calls(L, backward)
-    acc = {n: 0.0 for n, _ in calls}
-    for _ in range(2):
-        for _, f in calls:
-            f()
-    torch.cuda.synchronize()
-    for _ in range(reps):
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
-        evs[0].record()
+        evs[s][0].record()
         for i, (_, f) in enumerate(calls):
             f()
-            evs[i + 1].record()
-        torch.cuda.synchronize()
-        for i, (n, _) in enumerate(calls):
-            acc[n] += evs[i].elapsed_time(evs[i + 1])
-    return {n: v / reps for n, v in acc.items()}
+            evs[s][i + 1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    stages = {n: sum(evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(steps)) / steps
+              for i, (n, _) in enumerate(calls)}
+    return (t1 - t0) * 1e3 / steps, stages
 
 
-def algorithmic(wl, stats, slot_expert_np):
-    """Algorithmic bytes / flops per launch of each stage (documented with the roofline model)."""
+def algorithmic(wl, stats, slot_expert_np, L):
+    """Algorithmic work per launch of each stage: bytes for the bandwidth-bound stages (every input byte
+    read once, every output byte written once), flops for the two GEMMs plus the least HBM bytes they can
+    move (each operand read once, each output written once; wgrad's float32 gradient read and written)."""
     import numpy as np
     b = 4 if wl.dtype == "f32" else 2
     N, T, H = wl.N, wl.R * wl.S, wl.H
-    out = {
-        "plan_bytes": 8 * N,
-        "dispatch_bytes": T * H * b + N * H * b + 4 * N,
-    }
+    out = {"plan": 8 * N, "dispatch": T * H * b + N * H * b + 4 * N}
     if wl.Hp is not None:
         Hp = wl.Hp
-        copies_slotted = int(stats[1])
-        out["prefetch_bytes"] = 2 * H * Hp * b * copies_slotted
-        out["gemm_flops"] = 2 * N * H * Hp
-        out["combine_bytes"] = N * Hp * b + T * Hp * 4 + 8 * N
+        G = wl.E + wl.B
+        cu = L.cu_seqlens.cpu().numpy().reshape(wl.R, G + 1)
+        rows = np.diff(cu, axis=1)  # [R, E+B] rows per (rank, group)
+        home_used = int((rows[:, :wl.E].sum(axis=0) > 0).sum())
+        slots_used = int((rows[:, wl.E:] > 0).sum())
+        out["prefetch"] = 2 * H * Hp * b * int(stats[1])
+        out["group_gemm"] = 2 * N * H * Hp
+        out["group_gemm_min_bytes"] = N * H * b + (home_used + slots_used) * H * Hp * b + N * Hp * b
+        out["combine"] = N * Hp * b + T * Hp * 4 + 8 * N
         used = slot_expert_np[slot_expert_np >= 0]
-        experts_with_copies = len(np.unique(used))
-        out["reduce_grad_bytes"] = 4 * H * Hp * (2 * experts_with_copies + 2 * len(used))
-        out["wgrad_flops"] = 2 * N * H * Hp
+        out["reduce_grad"] = 4 * H * Hp * (2 * len(np.unique(used)) + 2 * len(used))
+        out["wgrad"] = 2 * N * H * Hp
+        out["wgrad_min_bytes"] = N * (H + Hp) * b + 8 * H * Hp * (home_used + slots_used)
     return out
+
+
+# library kernels of each stage (rocprofv3 base names) and the source file that holds them
+STAGE_KERNELS = {
+    "plan": ("plan_count", "plan_scan", "plan_solve", "plan_emit"),
+    "dispatch": ("dispatch_rows",),
+    "prefetch": ("prefetch_slots",),
+    "group_gemm": ("ggemm_tiles", "ggemm_bf16", "ggemm_generic"),
+    "combine": ("combine_vec", "combine_scalar"),
+    "wgrad": ("wgrad_schedule", "wgrad_bf16", "wgrad_generic"),
+    "reduce_grad": ("reduce_grad_kernel", "reduce_grad_scalar"),
+}
+STAGE_SOURCE = {"plan": "plan.hip", "dispatch": "move.hip", "prefetch": "move.hip", "group_gemm": "ggemm.hip",
+                "combine": "move.hip", "wgrad": "wgrad.hip", "reduce_grad": "move.hip"}
+CSRC = os.path.join(ROOT, "load_balanced_dispatch_amd", "csrc")
+
+
+def kernel_base(name):
+    """Base identifier of a demangled kernel name as rocprofv3 prints it."""
+    n = name.replace("(anonymous namespace)::", "")
+    if n.startswith("void "):
+        n = n[5:]
+    return re.split(r"[<(]", n, maxsplit=1)[0].rsplit("::", 1)[-1]
+
+
+def stage_of(base):
+    for st, ks in STAGE_KERNELS.items():
+        if base in ks:
+            return st
+    return None
+
+
+def sources_digest(stage):
+    """Hash of the source a stage's kernels are compiled from (its .hip file and every csrc header)."""
+    files = [os.path.join(CSRC, STAGE_SOURCE[stage])] + sorted(glob.glob(os.path.join(CSRC, "*.h")))
+    h = hashlib.sha256()
+    for f in files:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_path(wl):
+    return os.path.join(ROOT, "profiles", f"traffic_{wl.name}.md")
+
+
+def load_traffic(wl, target):
+    """HBM bytes per launch of each stage from the committed counter summary for this workload, or None for
+    a stage whose kernel source has changed since the counters were taken."""
+    path = traffic_path(wl)
+    if not os.path.exists(path):
+        return {}
+    text = open(path).read()
+    m = re.search(r"```json\n(.*?)\n```", text, re.S)
+    if not m:
+        return {}
+    rec = json.loads(m.group(1))
+    if rec.get("workload") != wl.name or rec.get("maxvio_target") != target:
+        return {}
+    return {st: (v["bytes_per_launch"] if v.get("sources") == sources_digest(st) else None)
+            for st, v in rec["stages"].items()}
+
+
+def stage_roofline(name, alg, ms, traffic, f32):
+    gemm = name in ("group_gemm", "wgrad")
+    if gemm:
+        bound, unit = ("alu", "TFLOP/s") if f32 else ("mfma", "TFLOP/s")
+        peak = MFMA_F32_VECTOR_TFLOPS if f32 else MFMA_BF16_PEAK_TFLOPS
+        achieved = alg[name] / (ms * 1e-3) / 1e12
+        per = f"{alg[name]:.4g} FLOP (2*N*H*H')"
+    else:
+        bound, unit, peak = "hbm", "GB/s", HBM_PEAK_GBS
+        achieved = alg[name] / (ms * 1e-3) / 1e9
+        per = f"{alg[name]:.4g} B"
+    t = traffic.get(name)
+    r = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+         "frac": round(achieved / peak, 4), "traffic": t, "avg_launch_ms": round(ms, 4),
+         "algorithmic_per_launch": per}
+    least = alg.get(name + "_min_bytes", alg[name] if not gemm else None)
+    if gemm:
+        r["least_bytes_per_launch"] = least
+    if t:
+        r["traffic_over_least_bytes"] = round(t / least, 3)
+    return r
+
+
+def stats_markdown(csv_path):
+    """Markdown table of the library kernels in a rocprofv3 --stats kernel summary (csv)."""
+    rows = list(csv.DictReader(open(csv_path)))
+    out = ["| kernel | stage | calls | avg us | min us | max us |", "|---|---|---|---|---|---|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        base = kernel_base(r["Name"])
+        st = stage_of(base)
+        if st is None:
+            continue
+        out.append(f"| `{base}` | {st} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    return "\n".join(out)
+
+
+def traffic_markdown(fetch_csv, write_csv, wl, target):
+    """Per-stage HBM bytes per launch from a FETCH_SIZE and a WRITE_SIZE counter run of --profile-pass,
+    each scaled by what the same counter reads for the closing 1 GiB device copy."""
+    def read(path, counter):
+        per, calib = {}, None
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            v, disp = float(r["Counter_Value"]), int(r["Dispatch_Id"])
+            base = kernel_base(r["Kernel_Name"])
+            if stage_of(base):
+                per.setdefault(base, []).append(v)
+            elif "copyBuffer" in r["Kernel_Name"] and (calib is None or disp > calib[0]):
+                calib = (disp, v)  # the last device copy is the 1 GiB calibration copy
+        return {k: sum(v) / len(v) for k, v in per.items()}, {k: len(v) for k, v in per.items()}, calib[1]
+    fetch, nf, cf = read(fetch_csv, "FETCH_SIZE")
+    write, nw, cw = read(write_csv, "WRITE_SIZE")
+    fs, ws = 1024 * 1024 / cf, 1024 * 1024 / cw  # KiB the 1 GiB copy should read / write, over the reading
+    stages = {}
+    lines = ["| stage | kernels | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes per launch (scaled) |",
+             "|---|---|---|---|---|---|"]
+    for st, ks in STAGE_KERNELS.items():
+        ks = [k for k in ks if k in fetch and k in write]
+        if not ks:
+            continue
+        f = sum(fetch[k] for k in ks)
+        w = sum(write[k] for k in ks)
+        b = f * 1024 * fs + w * 1024 * ws
+        stages[st] = {"kernels": ks, "fetch_kib": round(f, 1), "write_kib": round(w, 1),
+                      "bytes_per_launch": round(b), "dispatches": min(nf[k] for k in ks),
+                      "sources": sources_digest(st)}
+        lines.append(f"| {st} | {', '.join('`' + k + '`' for k in ks)} | {stages[st]['dispatches']} | "
+                     f"{f:.1f} | {w:.1f} | {b:.4g} |")
+    rec = {"workload": wl.name, "maxvio_target": target,
+           "calibration": {"copy_bytes": 1 << 30, "fetch_kib": cf, "write_kib": cw, "fetch_scale": round(fs, 4),
+                           "write_scale": round(ws, 4)},
+           "stages": stages}
+    return "\n".join(lines), rec
 
 
 def cpu_baseline(wl, seed, alpha, tokens_per_rank):
@@ -204,12 +334,7 @@ def main():
         print(json.dumps({"error": "this build measures one GPU only; multi-GPU runs are not part of it",
                           "n_gpus": args.gpus}))
         sys.exit(2)
-    import numpy as np
-    import torch
-
     from synthetic import WORKLOADS
-    from synthetic.calibrate import alpha_for
-    from synthetic.router import measured_maxvio
 
     wl = WORKLOADS[WORKLOAD_KEYS[args.workload]]
     backward = wl.Hp is not None and not args.forward_only
@@ -222,6 +347,23 @@ def main():
     else:
         head_target = None
         sweep_targets = []
+    if args.stats_md:
+        print(stats_markdown(args.stats_md))
+        return
+    if args.traffic_md:
+        table, rec = traffic_markdown(args.traffic_md[0], args.traffic_md[1], wl, head_target)
+        print(table)
+        print()
+        print("```json")
+        print(json.dumps(rec, indent=1))
+        print("```")
+        return
+
+    import numpy as np  # noqa: F401
+    import torch
+
+    from synthetic.calibrate import alpha_for
+    from synthetic.router import measured_maxvio
 
     def alpha_of(target):
         if wl.zipf_s is not None:
@@ -252,39 +394,32 @@ def main():
     for tgt in points:
         alpha = alpha_of(tgt)
         idx, _ = load_inputs(L, wl, args.seed, alpha)
-        ms, gemm_ms = time_steps(L, backward, args.steps if tgt == head_target else max(5, args.steps // 2),
-                                 args.warmup)
-        stages = time_stages(L, backward)
+        ms, stages = time_steps(L, backward, args.steps if tgt == head_target else max(5, args.steps // 2),
+                                args.warmup)
         torch.cuda.synchronize()
         stats = L.stats.cpu().numpy()
         slots = L.slot_expert.cpu().numpy()
-        results[tgt] = dict(alpha=alpha, maxvio=float(L.maxvio.item()), ms=ms, gemm_ms=gemm_ms, stages=stages,
+        results[tgt] = dict(alpha=alpha, maxvio=float(L.maxvio.item()), ms=ms, stages=stages,
                             stats=stats.tolist(), slots=slots, maxvio_host=measured_maxvio(idx, wl.E))
         log(f"maxvio target {tgt}: measured {results[tgt]['maxvio']:.3f}, {ms:.3f} ms/step, stages {stages}")
 
     h = results[head_target]
-    alg = algorithmic(wl, h["stats"], h["slots"])
+    alg = algorithmic(wl, h["stats"], h["slots"], L)
     st = h["stages"]
     comp = {"plan_dispatch_pairs_per_s": wl.N / ((st["plan"] + st["dispatch"]) * 1e-3),
-            "plan_ms": st["plan"], "dispatch_GBs": alg["dispatch_bytes"] / (st["dispatch"] * 1e-3) / 1e9}
-    roofline = None
+            "plan_ms": st["plan"], "dispatch_GBs": alg["dispatch"] / (st["dispatch"] * 1e-3) / 1e9}
     if wl.Hp is not None:
-        comp["group_gemm_tflops"] = alg["gemm_flops"] / (h["gemm_ms"] * 1e-3) / 1e12
-        comp["combine_GBs"] = alg["combine_bytes"] / (st["combine"] * 1e-3) / 1e9
-        comp["prefetch_GBs"] = alg["prefetch_bytes"] / (st["prefetch"] * 1e-3) / 1e9 if alg["prefetch_bytes"] else None
+        comp["group_gemm_tflops"] = alg["group_gemm"] / (st["group_gemm"] * 1e-3) / 1e12
+        comp["combine_GBs"] = alg["combine"] / (st["combine"] * 1e-3) / 1e9
+        comp["prefetch_GBs"] = alg["prefetch"] / (st["prefetch"] * 1e-3) / 1e9 if alg["prefetch"] else None
         if backward:
-            comp["wgrad_tflops"] = alg["wgrad_flops"] / (st["wgrad"] * 1e-3) / 1e12
-            comp["reduce_grad_GBs"] = (alg["reduce_grad_bytes"] / (st["reduce_grad"] * 1e-3) / 1e9
-                                       if alg["reduce_grad_bytes"] else None)
-        ach = comp["group_gemm_tflops"]
-        roofline = {"kernel": "ggemm_bf16 (moonep_group_gemm)", "bound": "mfma", "achieved": round(ach, 2),
-                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
-                    "traffic": None, "avg_launch_ms": round(h["gemm_ms"], 4),
-                    "algorithmic_per_launch": f"{alg['gemm_flops']:.4g} FLOP (2*N*H*H')"}
-    else:
-        ach = comp["dispatch_GBs"]
-        roofline = {"kernel": "dispatch_rows (moonep_dispatch)", "bound": "hbm", "achieved": round(ach, 1),
-                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+            comp["wgrad_tflops"] = alg["wgrad"] / (st["wgrad"] * 1e-3) / 1e12
+            comp["reduce_grad_GBs"] = (alg["reduce_grad"] / (st["reduce_grad"] * 1e-3) / 1e9
+                                       if alg["reduce_grad"] else None)
+    traffic = load_traffic(wl, head_target)
+    rooflines = {n: stage_roofline(n, alg, st[n], traffic, wl.dtype == "f32") for n in st}
+    dominant = max(st, key=lambda n: st[n])
+    roofline = dict(rooflines[dominant], stage=dominant)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -315,6 +450,7 @@ def main():
                    "copies_slotted_direct": h["stats"][:3]},
         "components": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in comp.items()},
         "roofline": roofline,
+        "rooflines": rooflines,
         "cpu_baseline": cpu,
         "sweep": sweep,
     }
