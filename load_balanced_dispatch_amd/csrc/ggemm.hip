@@ -10,7 +10,8 @@
 //   * ggemm_tiles (one block) turns cu_seqlens into a prefix of 256-row M-tiles per
 //     (rank, group), in device memory, so the GEMM needs no host sync.
 //   * fwd::ggemm_bf16 is persistent (one 512-thread block per CU), 256 x 256 x 32 block tiles,
-//     eight waves of 128 x 64 with MFMA 32x32x16 bf16.  Operands stream global -> LDS with
+//     eight waves of 128 x 64 with MFMA 32x32x16 bf16 in two ping-pong groups (one computes while
+//     the other loads).  Operands stream global -> LDS with
 //     global_load_lds_dwordx4 into a 4-stage ring; the activation operand (k contiguous) is read
 //     with ds_read_b128, the weight operand (k along LDS rows, as the [H, H'] layout stores it)
 //     with ds_read_b64_tr_b16; both LDS layouts are XOR-swizzled against bank conflicts.  The
@@ -95,6 +96,7 @@ __device__ __forceinline__ int find_group(const int32_t* tstart, int NG, int mt)
 
 namespace fwd {
 constexpr int BM = 256, BN = 256, BK = 32, STAGES = 4, NWAVES = 8;
+constexpr int OPS = 4;  // DMA instructions per wave per stage (2 for A, 2 for B)
 constexpr int A_STAGE = BM * BK;  // 64-byte rows; 16-byte chunks XOR-swizzled by row
 constexpr int B_STAGE = BK * BN;  // 512-byte rows; 64-byte blocks XOR-swizzled by row
 constexpr int STAGE = A_STAGE + B_STAGE;
@@ -150,7 +152,6 @@ __global__ __launch_bounds__(512, 1) void ggemm_bf16(const uint16_t* __restrict_
     const int width = min(BN, Hp - n0);
     const int strips = min(TM, max(0, (rows - wm * 128 + 31) / 32));  // valid 32-row strips of this wave
     const bool wave_cols = wn * WN < width;
-    const bool full = strips == TM && wave_cols;
 
     // global sources of this wave's four DMA instructions per stage (2 for A, 2 for B)
     const uint16_t* a_src[2];
@@ -205,49 +206,52 @@ __global__ __launch_bounds__(512, 1) void ggemm_bf16(const uint16_t* __restrict_
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
     };
-    // stage 0 ready
-    if (KT > 2) wait_vmcnt<8>();
-    else if (KT > 1) wait_vmcnt<4>();
-    else wait_vmcnt<0>();
-    lds_barrier();
-    if (full) {
-      // the barrier sits between the two k-steps of a stage, so every LDS read overlaps MFMAs:
-      // reads of (kt, 1) run under the MFMAs of (kt, 0), reads of (kt+1, 0) under those of (kt, 1)
-      bf16x8 a0[TM], b0[TN], a1[TM], b1[TN];
-      frag(0, 0, a0, b0);
-      for (int kt = 0; kt < KT; ++kt) {
-        frag(kt, 1, a1, b1);
-        mma(a0, b0);
-        if (kt + 1 < KT) {
-          if (kt + 2 < KT) wait_vmcnt<4>();
-          else wait_vmcnt<0>();
-          lds_barrier();  // stage kt+1 landed everywhere; every wave is done with stage kt-1
-          if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1);
-          frag(kt + 1, 0, a0, b0);
-        }
-        mma(a1, b1);
+    // Ping-pong: waves 0-3 (group A, one per SIMD) and 4-7 (group B, the other wave of each SIMD)
+    // alternate between a memory phase (the operands of one stage, LDS -> registers, plus this
+    // wave's share of the DMA three stages ahead) and a compute phase (that stage's 16 MFMAs), half
+    // a stage apart, so while one wave of a SIMD waits on LDS the other keeps the MFMA pipe busy.
+    // Phase q opens with a barrier.  A: memory(t) in phase 2t, compute(t) in 2t+1; B: memory(t) in
+    // 2t+1, compute(t) in 2t+2; 2*KT + 1 phases.  memory(t) refills the slot of stage t-1, which B
+    // read in phase 2t-1.  A tile at a group's end computes all its strips (rows past the end load
+    // the group's last row); the epilogue stores only the valid rows.
+    bf16x8 fa[KK][TM], fb[KK][TN];
+    auto mem = [&](int t) {
+      if (wave_cols) {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) frag(t, kk, fa[kk], fb[kk]);
       }
+      if (t + STAGES - 1 < KT) issue(t + STAGES - 1);
+    };
+    auto comp = [&]() {
+      if (wave_cols) {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) mma(fa[kk], fb[kk]);
+      }
+    };
+    // barrier opening phase 2t: this wave has issued the stages up to min(t + 2, KT - 1), so
+    // waiting until only the later ones are in flight means its share of stage t has landed, and
+    // the barrier extends that to every wave's share
+    auto even_barrier = [&](int t) {
+      if (t + 2 < KT) wait_vmcnt<2 * OPS>();
+      else if (t + 1 < KT) wait_vmcnt<OPS>();
+      else wait_vmcnt<0>();
+      lds_barrier();
+    };
+    if (w < 4) {
+      for (int t = 0; t < KT; ++t) {
+        even_barrier(t);
+        mem(t);
+        lds_barrier();
+        comp();
+      }
+      even_barrier(KT);
     } else {
-      for (int kt = 0; kt < KT; ++kt) {
-        if (kt > 0) {  // stage kt landed everywhere; every wave is done with stage kt-1
-          if (kt + 2 < KT) wait_vmcnt<8>();
-          else if (kt + 1 < KT) wait_vmcnt<4>();
-          else wait_vmcnt<0>();
-          lds_barrier();
-        }
-        if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1);
-        if (wave_cols) {
-#pragma unroll
-          for (int kk = 0; kk < KK; ++kk) {
-            bf16x8 a[TM], b[TN];
-            frag(kt, kk, a, b);
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-              if (i < strips)
-#pragma unroll
-                for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
-          }
-        }
+      even_barrier(0);
+      for (int t = 0; t < KT; ++t) {
+        lds_barrier();
+        mem(t);
+        even_barrier(t + 1);
+        comp();
       }
     }
     lds_barrier();  // the ring is free: every wave has read its last stage
