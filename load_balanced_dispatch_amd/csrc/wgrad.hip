@@ -260,31 +260,61 @@ __global__ __launch_bounds__(512, 1) void wgrad_bf16(const uint16_t* __restrict_
       for (int j = 0; j < TN; ++j) acc[i][j] = (f32x16)(0.f);
 
     for (int st = 0; st < STAGES - 1 && st < nchunks; ++st) issue_next();
-    for (int kt = 0; kt < nchunks; ++kt) {
-      if (kt + 2 < nchunks) wait_vmcnt<8>();
-      else if (kt + 1 < nchunks) wait_vmcnt<4>();
-      else wait_vmcnt<0>();
-      lds_barrier();
-      if (issued < nchunks) issue_next();
-      const uint16_t* Xs = lds + (kt % STAGES) * STAGE;
+    // Ping-pong, as in the forward group GEMM: waves 0-3 and 4-7 (one of each per SIMD) alternate
+    // half a chunk apart between a memory phase (one chunk's operands LDS -> registers, plus this
+    // wave's share of the DMA three chunks ahead) and a compute phase (that chunk's 16 MFMAs).
+    // Phase q opens with a barrier; A: memory(t) in phase 2t, compute(t) in 2t+1; B: memory(t) in
+    // 2t+1, compute(t) in 2t+2.  memory(t) refills the slot of chunk t-1, which B read in 2t-1.
+    const int KT = nchunks;
+    bf16x8 fa[KK][TM], fb[KK][TN];
+    auto mem = [&](int t) {
+      const uint16_t* Xs = lds + (t % STAGES) * STAGE;
       const uint16_t* Ds = Xs + X_STAGE;
       if (wave_cols) {
-        bf16x8 a[2][TM], b[2][TN];
-        auto frag = [&](int kk, bf16x8 (&fa)[TM], bf16x8 (&fb)[TN]) {
-#pragma unroll
-          for (int j = 0; j < TN; ++j) fb[j] = operand_rows(Ds, kk * 16, wn * WN + j * 32, lane);
-#pragma unroll
-          for (int i = 0; i < TM; ++i) fa[i] = operand_rows(Xs, kk * 16, wm * 128 + i * 32, lane);
-        };
-        frag(0, a[0], b[0]);
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-          if (kk + 1 < KK) frag(kk + 1, a[(kk + 1) & 1], b[(kk + 1) & 1]);
+#pragma unroll
+          for (int j = 0; j < TN; ++j) fb[kk][j] = operand_rows(Ds, kk * 16, wn * WN + j * 32, lane);
+#pragma unroll
+          for (int i = 0; i < TM; ++i) fa[kk][i] = operand_rows(Xs, kk * 16, wm * 128 + i * 32, lane);
+        }
+      }
+      if (issued < nchunks) issue_next();
+    };
+    auto comp = [&]() {
+      if (wave_cols) {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
           for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(a[kk & 1][i], b[kk & 1][j], acc[i][j]);
-        }
+            for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(fa[kk][i], fb[kk][j], acc[i][j]);
+      }
+    };
+    // barrier opening phase 2t: this wave has issued chunks up to min(t + 2, KT - 1); waiting until
+    // only the later ones are in flight means its share of chunk t has landed, and the barrier
+    // extends that to every wave's share
+    auto even_barrier = [&](int t) {
+      if (t + 2 < KT) wait_vmcnt<8>();
+      else if (t + 1 < KT) wait_vmcnt<4>();
+      else wait_vmcnt<0>();
+      lds_barrier();
+    };
+    if (w < 4) {
+      for (int t = 0; t < KT; ++t) {
+        even_barrier(t);
+        mem(t);
+        lds_barrier();
+        comp();
+      }
+      even_barrier(KT);
+    } else {
+      even_barrier(0);
+      for (int t = 0; t < KT; ++t) {
+        lds_barrier();
+        mem(t);
+        even_barrier(t + 1);
+        comp();
       }
     }
     lds_barrier();
@@ -303,18 +333,26 @@ __global__ __launch_bounds__(512, 1) void wgrad_bf16(const uint16_t* __restrict_
       }
       __syncthreads();
       if (wave_cols) {
-        constexpr int CPR = WN / 4;
+        // all eight 16-byte reads of this wave's part of the strip are issued before any write,
+        // so they are in flight together instead of one read-modify-write round trip at a time
+        constexpr int CPR = WN / 4, NQ = 32 * CPR / 64;
+        f32x4* p[NQ];
+        f32x4 v[NQ];
 #pragma unroll
-        for (int q = lane; q < 32 * CPR; q += 64) {
-          const int rr = q / CPR, cc = q % CPR;
-          f32x4* p = reinterpret_cast<f32x4*>(out + (int64_t)(h0 + wm * 128 + i * 32 + rr) * Hp + n0 + wn * WN + cc * 4);
+        for (int u = 0; u < NQ; ++u) {
+          const int q = lane + 64 * u, rr = q / CPR, cc = q % CPR;
+          p[u] = reinterpret_cast<f32x4*>(out + (int64_t)(h0 + wm * 128 + i * 32 + rr) * Hp + n0 + wn * WN + cc * 4);
+          v[u] = *p[u];
+        }
+#pragma unroll
+        for (int u = 0; u < NQ; ++u) {
+          const int q = lane + 64 * u, rr = q / CPR, cc = q % CPR;
           const f32x4 s = *reinterpret_cast<const f32x4*>(stage + rr * SP + cc * 4);
-          f32x4 v = *p;
-          v[0] = v[0] + s[0];
-          v[1] = v[1] + s[1];
-          v[2] = v[2] + s[2];
-          v[3] = v[3] + s[3];
-          *p = v;
+          v[u][0] = v[u][0] + s[0];
+          v[u][1] = v[u][1] + s[1];
+          v[u][2] = v[u][2] + s[2];
+          v[u][3] = v[u][3] + s[3];
+          *p[u] = v[u];
         }
       }
       __syncthreads();
