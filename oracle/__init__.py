@@ -18,8 +18,10 @@ Sources (web pages about MoonEP):
 Modules:
   planner   -- histogram, maxvio, and the home-first prefix-sum planner, step by
                step (a heuristic, so the oracle follows its steps).
-  layer     -- dispatch, prefetch, group GEMM, combine, wgrad, reduce_grad, and
-               the plain MoE definitions they must reproduce.
+  layer     -- dispatch, prefetch, group GEMM, combine, wgrad, reduce_grad, the
+               backward of the data path (combine backward, group-GEMM dgrad,
+               dispatch backward), and the plain MoE definitions (forward and
+               gradients) they must reproduce.
   mincopies -- brute-force minimum number of redundant copies on tiny inputs.
 
 Parity status: every function here is pinned by a ``-m "not gpu"`` test

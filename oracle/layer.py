@@ -1,4 +1,4 @@
-"""Oracle: the data-moving and arithmetic stages of the layer (test infrastructure).
+"""Oracle: the data-moving and arithmetic stages of the layer, forward and backward (test infrastructure).
 
 Plain numpy, float64 arithmetic on whatever values the caller passes (the
 tests pass bf16-rounded inputs converted to float64).
@@ -152,6 +152,71 @@ def reduce_grad(slot_expert, dW_home, dW_slots, dtype=np.float64):
     return dW_home, dW_slots
 
 
+# ------------------------------------------------------------------ backward of the data path
+#
+# The pages say the backward pass runs through the same buffers and that the gradients of the
+# redundant experts are folded back to their home experts ([P2] "Core technique"; [P3] third
+# paragraph); they say nothing more about the data gradients.  Read plainly, these are the chain
+# rule of dispatch -> group GEMM -> combine, each the transpose of its forward stage.
+
+def combine_backward(dout: np.ndarray, Yp: np.ndarray, dest_idx: np.ndarray, gates: np.ndarray):
+    """Gradients of out = combine(Yp, dest_idx, gates) given dout = d(loss)/d(out):
+
+    dYp[dest_idx[r,s,k]] = gate[r,s,k] * dout[r,s]   (every row of Yp is the destination of one pair)
+    dgate[r,s,k] = sum_n dout[r,s,n] * Yp[dest_idx[r,s,k], n]
+    """
+    R, S, K = dest_idx.shape
+    D = dout.shape[2]
+    dflat = np.asarray(dest_idx).reshape(R * S, K)
+    gf = np.asarray(gates, dtype=np.float64).reshape(R * S, K)
+    do = np.asarray(dout, dtype=np.float64).reshape(R * S, D)
+    dYp = np.zeros((Yp.shape[0], D), dtype=np.float64)
+    dgate = np.zeros((R * S, K), dtype=np.float64)
+    for k in range(K):
+        dYp[dflat[:, k]] = gf[:, k:k + 1] * do
+        dgate[:, k] = np.sum(do * Yp[dflat[:, k]].astype(np.float64), axis=1)
+    return dYp, dgate.reshape(R, S, K)
+
+
+def group_gemm_dgrad(dYp, W_home, W_slots, cu_seqlens, P: int, rows=None) -> np.ndarray:
+    """dXp[rows of group g on rank r] = dYp[those rows] @ W_r[g]^T: the gradient of the VM group GEMM
+    with respect to its input, through the same groups and the same weight rows (home or slot).
+
+    With ``rows`` given, returns only those output rows.
+    """
+    R = cu_seqlens.shape[0]
+    G = cu_seqlens.shape[1] - 1
+    H = W_home.shape[1]
+    if rows is None:
+        dX = np.zeros((dYp.shape[0], H), dtype=np.float64)
+        for r in range(R):
+            for g in range(G):
+                a, b = r * P + cu_seqlens[r, g], r * P + cu_seqlens[r, g + 1]
+                if b > a:
+                    dX[a:b] = dYp[a:b].astype(np.float64) @ rank_weight(W_home, W_slots, r, g).astype(np.float64).T
+        return dX
+    ranks, groups = row_group(cu_seqlens, P, rows)
+    dX = np.zeros((len(rows), H), dtype=np.float64)
+    for i, (row, r, g) in enumerate(zip(rows, ranks, groups)):
+        dX[i] = rank_weight(W_home, W_slots, r, g).astype(np.float64) @ dYp[row].astype(np.float64)
+    return dX
+
+
+def dispatch_backward(dXp: np.ndarray, dest_idx: np.ndarray, tokens=None) -> np.ndarray:
+    """Gradient of the fused permute: dX[r,s] = sum_k dXp[dest_idx[r,s,k]], k ascending.
+
+    ``tokens`` (flat r*S+s ids) restricts the result to those tokens.
+    """
+    R, S, K = dest_idx.shape
+    H = dXp.shape[1]
+    dflat = np.asarray(dest_idx).reshape(R * S, K)
+    tok = np.arange(R * S) if tokens is None else np.asarray(tokens)
+    dX = np.zeros((len(tok), H), dtype=np.float64)
+    for k in range(K):
+        dX += dXp[dflat[tok, k]].astype(np.float64)
+    return dX if tokens is not None else dX.reshape(R, S, H)
+
+
 # ------------------------------------------------------------------ plain definitions
 
 def moe_forward(X, W_home, topk_idx, gates, tokens=None) -> np.ndarray:
@@ -182,3 +247,25 @@ def expert_weight_grad(X, dY_of_pair, topk_idx, E: int) -> np.ndarray:
         if len(q):
             dW[e] = Xf[q // K].T @ dY_of_pair[q].astype(np.float64)
     return dW
+
+
+def moe_backward(X, W_home, topk_idx, gates, dout):
+    """Plain gradients of moe_forward given dout:
+
+    dX[r,s] = sum_k gate[r,s,k] * W[e] @ dout[r,s]      (e = topk_idx[r,s,k])
+    dgate[r,s,k] = dout[r,s] . (X[r,s] @ W[e])
+    """
+    R, S, H = X.shape
+    K = topk_idx.shape[2]
+    Xf = X.reshape(R * S, H).astype(np.float64)
+    ids = np.asarray(topk_idx).reshape(R * S, K)
+    gf = np.asarray(gates, dtype=np.float64).reshape(R * S, K)
+    do = np.asarray(dout, dtype=np.float64).reshape(R * S, -1)
+    dX = np.zeros((R * S, H), dtype=np.float64)
+    dgate = np.zeros((R * S, K), dtype=np.float64)
+    for t in range(R * S):
+        for k in range(K):
+            w = W_home[ids[t, k]].astype(np.float64)
+            dX[t] += gf[t, k] * (w @ do[t])
+            dgate[t, k] = do[t] @ (Xf[t] @ w)
+    return dX.reshape(R, S, H), dgate.reshape(R, S, K)
