@@ -163,6 +163,49 @@ int moonep_group_gemm(moonep_dims d, int32_t H, int32_t Hp, moonep_dtype t, cons
 int moonep_combine(moonep_dims d, int32_t D, moonep_dtype t, const void* Yp, const int32_t* dest_idx,
                    const float* gates, float* out, moonep_stream stream);
 
+/*
+ * Backward of the data path.  The pages state that the backward pass runs through the same
+ * buffers and that redundant experts' gradients go back to their home experts ([P2] "Core
+ * technique"; [P3] third paragraph); read plainly, the data gradients are the chain rule of
+ * dispatch -> group GEMM -> combine, each stage the transpose of its forward.
+ */
+
+/*
+ * moonep_combine_backward -- gradients of moonep_combine given dout = d(loss)/d(out).
+ *   For every pair (r,s,k) with q = dest_idx[r,s,k]:
+ *     dYp[q] = gates[r,s,k] * dout[r,s]            (float32 product, then rounded to dtype t)
+ *     dgates[r,s,k] = sum_n dout[r,s,n] * Yp[q,n]  (float32 accumulation)
+ *   Every row of dYp is the destination of exactly one pair, so all of dYp is written.
+ * In:  dout [R,S,D] float32;  Yp [R*S*K,D] dtype t;  dest_idx [R,S,K] int32;  gates [R,S,K] float32.
+ * Out: dYp [R*S*K,D] dtype t;  dgates [R,S,K] float32.
+ */
+int moonep_combine_backward(moonep_dims d, int32_t D, moonep_dtype t, const float* dout, const void* Yp,
+                            const int32_t* dest_idx, const float* gates, void* dYp, float* dgates,
+                            moonep_stream stream);
+
+/*
+ * moonep_group_gemm_dgrad -- gradient of the VM group GEMM with respect to its input, through the
+ * same groups and the same weight rows (home, slot, or a home row read directly):
+ *   For rank r, group g: dXp[rows] = dYp[rows] @ W_r[g]^T, rows = r*P + [cu[r,g], cu[r,g+1]).
+ *   bf16: float32 accumulation, result rounded to nearest-even bf16;  f32: float32 throughout.
+ * In:  dYp [R*S*K,Hp], W_home [E,H,Hp], W_slots [R,B,H,Hp] (NULL when B == 0), dtype t;
+ *      cu_seqlens [R,E+B+1] int32.
+ * Out: dXp [R*S*K,H] dtype t.
+ * workspace: moonep_group_gemm_workspace_bytes(d) bytes (the same workspace as the forward).
+ */
+int moonep_group_gemm_dgrad(moonep_dims d, int32_t H, int32_t Hp, moonep_dtype t, const void* dYp,
+                            const void* W_home, const void* W_slots, const int32_t* cu_seqlens, void* dXp,
+                            void* workspace, moonep_stream stream);
+
+/*
+ * moonep_dispatch_backward -- gradient of moonep_dispatch (the fused permute):
+ *   dX[r,s] = sum over k ascending of dXp[dest_idx[r,s,k]], float32 additions.
+ * In:  dXp [R*S*K,H] dtype t;  dest_idx [R,S,K] int32.
+ * Out: dX [R,S,H] float32.
+ */
+int moonep_dispatch_backward(moonep_dims d, int32_t H, moonep_dtype t, const void* dXp, const int32_t* dest_idx,
+                             float* dX, moonep_stream stream);
+
 /* Bytes of device workspace moonep_wgrad needs. */
 size_t moonep_wgrad_workspace_bytes(moonep_dims d);
 

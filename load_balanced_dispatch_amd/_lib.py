@@ -65,6 +65,9 @@ def _load():
         "moonep_wgrad_workspace_bytes": (sz, [Dims]),
         "moonep_wgrad": (ctypes.c_int, [Dims, i32, i32, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp]),
         "moonep_reduce_grad": (ctypes.c_int, [Dims, i32, i32, vp, vp, vp, vp]),
+        "moonep_combine_backward": (ctypes.c_int, [Dims, i32, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp]),
+        "moonep_group_gemm_dgrad": (ctypes.c_int, [Dims, i32, i32, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp]),
+        "moonep_dispatch_backward": (ctypes.c_int, [Dims, i32, ctypes.c_int, vp, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -78,7 +81,8 @@ _LIB = _load()
 # exported symbol names, as declared in include/moonep.h
 SYMBOLS = ("moonep_last_error", "moonep_plan_workspace_bytes", "moonep_plan", "moonep_dispatch", "moonep_prefetch",
            "moonep_group_gemm_workspace_bytes", "moonep_group_gemm", "moonep_combine",
-           "moonep_wgrad_workspace_bytes", "moonep_wgrad", "moonep_reduce_grad")
+           "moonep_wgrad_workspace_bytes", "moonep_wgrad", "moonep_reduce_grad", "moonep_combine_backward",
+           "moonep_group_gemm_dgrad", "moonep_dispatch_backward")
 
 
 def lib():
@@ -227,3 +231,36 @@ def moonep_reduce_grad(d: Dims, H: int, Hp: int, slot_expert, dW_home, dW_slots,
                                    _ptr(dW_home, "dW_home", torch.float32, d.E * H * Hp),
                                    _ptr(dW_slots, "dW_slots", torch.float32, d.R * d.B * H * Hp, optional=d.B == 0),
                                    _stream(stream)))
+
+
+def moonep_combine_backward(d: Dims, D: int, dout, Yp, dest_idx, gates, dYp, dgates, stream=None):
+    import torch
+    t = _dtype_enum(Yp)
+    _check(_LIB.moonep_combine_backward(d, int(D), t, _ptr(dout, "dout", torch.float32, d.R * d.S * D),
+                                        _ptr(Yp, "Yp", Yp.dtype, d.N * D),
+                                        _ptr(dest_idx, "dest_idx", torch.int32, d.N),
+                                        _ptr(gates, "gates", torch.float32, d.N),
+                                        _ptr(dYp, "dYp", Yp.dtype, d.N * D),
+                                        _ptr(dgates, "dgates", torch.float32, d.N), _stream(stream)))
+
+
+def moonep_group_gemm_dgrad(d: Dims, H: int, Hp: int, dYp, W_home, W_slots, cu_seqlens, dXp, workspace,
+                            stream=None):
+    import torch
+    t = _dtype_enum(dYp)
+    if workspace.numel() * workspace.element_size() < moonep_group_gemm_workspace_bytes(d):
+        raise ValueError("group GEMM workspace too small")
+    _check(_LIB.moonep_group_gemm_dgrad(d, int(H), int(Hp), t, _ptr(dYp, "dYp", dYp.dtype, d.N * Hp),
+                                        _ptr(W_home, "W_home", dYp.dtype, d.E * H * Hp),
+                                        _ptr(W_slots, "W_slots", dYp.dtype, d.R * d.B * H * Hp, optional=d.B == 0),
+                                        _ptr(cu_seqlens, "cu_seqlens", torch.int32, d.R * (d.E + d.B + 1)),
+                                        _ptr(dXp, "dXp", dYp.dtype, d.N * H), _ptr(workspace, "workspace"),
+                                        _stream(stream)))
+
+
+def moonep_dispatch_backward(d: Dims, H: int, dXp, dest_idx, dX, stream=None):
+    import torch
+    t = _dtype_enum(dXp)
+    _check(_LIB.moonep_dispatch_backward(d, int(H), t, _ptr(dXp, "dXp", dXp.dtype, d.N * H),
+                                         _ptr(dest_idx, "dest_idx", torch.int32, d.N),
+                                         _ptr(dX, "dX", torch.float32, d.R * d.S * H), _stream(stream)))

@@ -114,6 +114,13 @@ __device__ __forceinline__ int a_off(int row, int c) { return row * BK + 8 * (c 
 // four rows a transpose read touches land in different banks.
 __device__ __forceinline__ int b_off(int k, int n) { return k * BN + ((((n >> 5) ^ (k & 3)) << 5) | (n & 31)); }
 
+// C[rows of (r, g)] = A[those rows] @ op(W_r[g]), every W_r[g] an [H, H'] row-major matrix:
+//   forward (BT = false): A = Xp [N, H], op(W) = W, C = Yp [N, H']  (K = H,  N = H')
+//   dgrad   (BT = true):  A = dYp [N, H'], op(W) = W^T, C = dXp [N, H] (K = H', N = H)
+// With BT the weight tile is stored n-major (each output column's k-run is 64 contiguous bytes of a
+// W row), so it is staged and read exactly like the activation tile; otherwise it is k-major and
+// read with the transpose read.
+//
 // Persistent: one 512-thread block per CU; tile ids are remapped so the blocks of one XCD
 // (workgroups are dealt to the 8 XCDs round-robin) take consecutive tiles, which share token rows
 // and expert weights in that XCD's L2.  Block tile 256 x 256 x 32; eight waves of 128 x 64
@@ -121,6 +128,7 @@ __device__ __forceinline__ int b_off(int k, int n) { return k * BN + ((((n >> 5)
 // global_load_lds_dwordx4 into a 4-stage ring, three stages ahead of the MFMAs, with no
 // register staging.  The last n-tile may be narrower than 256 (H' % 256 != 0): its missing
 // columns load a repeated valid column and their waves skip MFMAs and stores.
+template <bool BT>
 __global__ __launch_bounds__(512, 1) void ggemm_bf16(const uint16_t* __restrict__ Xp,
                                                      const uint16_t* __restrict__ W_home,
                                                      const uint16_t* __restrict__ W_slots,
@@ -128,14 +136,15 @@ __global__ __launch_bounds__(512, 1) void ggemm_bf16(const uint16_t* __restrict_
                                                      const int32_t* __restrict__ tstart, uint16_t* __restrict__ Yp,
                                                      int R, int E, int B, int P, int H, int Hp) {
   __shared__ __attribute__((aligned(1024))) uint16_t lds[LDS_ELEMS];
+  const int K = BT ? Hp : H, N = BT ? H : Hp;  // reduction length and output width
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int wm = w >> 2, wn = w & 3;
   const int G = E + B, G1 = G + 1, NG = R * G;
-  const int NT = (Hp + BN - 1) / BN;
+  const int NT = (N + BN - 1) / BN;
   const int total = tstart[NG] * NT;
   const int nblk = gridDim.x;
   const int vb = (nblk % 8 == 0) ? (int)(blockIdx.x % 8) * (nblk / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
-  const int KT = H / BK;
+  const int KT = K / BK;
   const int a_lr = lane >> 2, a_ls = lane & 3;   // A: one wave instruction fills 16 rows
   const int b_lr = lane >> 5, b_ls = lane & 31;  // B: one wave instruction fills 2 rows
 
@@ -149,7 +158,7 @@ __global__ __launch_bounds__(512, 1) void ggemm_bf16(const uint16_t* __restrict_
     const int64_t row0 = (int64_t)r * P + c0 + mo;
     const uint16_t* Wg = g < E ? W_home + (int64_t)g * H * Hp : W_slots + ((int64_t)r * B + (g - E)) * H * Hp;
     const int n0 = nt * BN;
-    const int width = min(BN, Hp - n0);
+    const int width = min(BN, N - n0);
     const int strips = min(TM, max(0, (rows - wm * 128 + 31) / 32));  // valid 32-row strips of this wave
     const bool wave_cols = wn * WN < width;
 
@@ -158,21 +167,27 @@ __global__ __launch_bounds__(512, 1) void ggemm_bf16(const uint16_t* __restrict_
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int row = (2 * w + i) * 16 + a_lr;  // rows past the group end repeat its last row
-      a_src[i] = Xp + (row0 + min(row, rows - 1)) * H + 8 * (a_ls ^ a_swz(row));
+      a_src[i] = Xp + (row0 + min(row, rows - 1)) * K + 8 * (a_ls ^ a_swz(row));
     }
     const uint16_t* b_src[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int k = (2 * w + i) * 2 + b_lr;
-      const int q = (b_ls >> 2) ^ (k & 3);
-      b_src[i] = Wg + (int64_t)k * Hp + min(n0 + (q * 4 + (b_ls & 3)) * 8, Hp - 8);
+      if (BT) {  // output columns past N repeat the last one
+        const int row = (2 * w + i) * 16 + a_lr;
+        b_src[i] = Wg + (int64_t)min(n0 + row, N - 1) * Hp + 8 * (a_ls ^ a_swz(row));
+      } else {
+        const int k = (2 * w + i) * 2 + b_lr;
+        const int q = (b_ls >> 2) ^ (k & 3);
+        b_src[i] = Wg + (int64_t)k * Hp + min(n0 + (q * 4 + (b_ls & 3)) * 8, Hp - 8);
+      }
     }
+    const int64_t b_step = BT ? BK : (int64_t)BK * Hp;  // one stage along k
     auto issue = [&](int kt) {
       uint16_t* st = lds + (kt % STAGES) * STAGE;
 #pragma unroll
       for (int i = 0; i < 2; ++i) dma16(a_src[i] + kt * BK, st + (2 * w + i) * 512);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) dma16(b_src[i] + (int64_t)kt * BK * Hp, st + A_STAGE + (2 * w + i) * 512);
+      for (int i = 0; i < 2; ++i) dma16(b_src[i] + kt * b_step, st + A_STAGE + (2 * w + i) * 512);
     };
 
     f32x16 acc[TM][TN];
@@ -187,12 +202,17 @@ __global__ __launch_bounds__(512, 1) void ggemm_bf16(const uint16_t* __restrict_
       const uint16_t* Bs = As + A_STAGE;
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int grp4 = lane >> 4, c = lane & 15;
-        const int n = wn * WN + j * 32 + 16 * (grp4 & 1) + 4 * (c & 3);
-        const int k = kk * 16 + 8 * (grp4 >> 1) + (c >> 2);
-        const bf16x4 lo = lds_tr4(Bs + b_off(k, n));
-        const bf16x4 hi = lds_tr4(Bs + b_off(k + 4, n));
-        b[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        if (BT) {
+          const int n = wn * WN + j * 32 + (lane & 31);
+          b[j] = *reinterpret_cast<const bf16x8*>(Bs + a_off(n, kk * 2 + (lane >> 5)));
+        } else {
+          const int grp4 = lane >> 4, c = lane & 15;
+          const int n = wn * WN + j * 32 + 16 * (grp4 & 1) + 4 * (c & 3);
+          const int k = kk * 16 + 8 * (grp4 >> 1) + (c >> 2);
+          const bf16x4 lo = lds_tr4(Bs + b_off(k, n));
+          const bf16x4 hi = lds_tr4(Bs + b_off(k + 4, n));
+          b[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
       }
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
@@ -278,7 +298,7 @@ __global__ __launch_bounds__(512, 1) void ggemm_bf16(const uint16_t* __restrict_
           const int rr = q / CPR, cc = q % CPR;
           const int row = wm * 128 + i * 32 + rr;
           if (row < rows)
-            *reinterpret_cast<u32x4*>(Yp + (row0 + row) * Hp + n0 + wn * WN + cc * 8) =
+            *reinterpret_cast<u32x4*>(Yp + (row0 + row) * N + n0 + wn * WN + cc * 8) =
                 *reinterpret_cast<const u32x4*>(stage + rr * SP + cc * 8);
         }
       }
@@ -304,7 +324,7 @@ __device__ __forceinline__ void store_elem<float>(float* p, float v) { *p = v; }
 template <>
 __device__ __forceinline__ void store_elem<uint16_t>(uint16_t* p, float v) { *p = f32_to_bf16(v); }
 
-template <typename T>
+template <typename T, bool BT>
 __global__ __launch_bounds__(256) void ggemm_generic(const T* __restrict__ Xp, const T* __restrict__ W_home,
                                                      const T* __restrict__ W_slots, const int32_t* __restrict__ cu,
                                                      const int32_t* __restrict__ tstart, T* __restrict__ Yp, int R,
@@ -312,8 +332,9 @@ __global__ __launch_bounds__(256) void ggemm_generic(const T* __restrict__ Xp, c
   __shared__ float As[kGenBK][kGenBM + 4];
   __shared__ float Bs[kGenBK][kGenBN + 4];
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int K = BT ? Hp : H, N = BT ? H : Hp;  // reduction length and output width (as in ggemm_bf16)
   const int G = E + B, G1 = G + 1, NG = R * G;
-  const int NT = (Hp + kGenBN - 1) / kGenBN;
+  const int NT = (N + kGenBN - 1) / kGenBN;
   const int total = tstart[NG] * NT;
   for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
     const int mt = tile / NT, nt = tile % NT;
@@ -326,14 +347,15 @@ __global__ __launch_bounds__(256) void ggemm_generic(const T* __restrict__ Xp, c
     const T* Wg = g < E ? W_home + (int64_t)g * H * Hp : W_slots + ((int64_t)r * B + (g - E)) * H * Hp;
     const int n0 = nt * kGenBN;
     float acc[4][4] = {};
-    for (int k0 = 0; k0 < H; k0 += kGenBK) {
+    for (int k0 = 0; k0 < K; k0 += kGenBK) {
       for (int i = threadIdx.x; i < kGenBK * kGenBM; i += 256) {
         const int m = i / kGenBK, k = i % kGenBK;
-        As[k][m] = (m < rows && k0 + k < H) ? load_elem(Xp + (row0 + m) * H + k0 + k) : 0.f;
+        As[k][m] = (m < rows && k0 + k < K) ? load_elem(Xp + (row0 + m) * K + k0 + k) : 0.f;
       }
       for (int i = threadIdx.x; i < kGenBK * kGenBN; i += 256) {
         const int k = i / kGenBN, n = i % kGenBN;
-        Bs[k][n] = (k0 + k < H && n0 + n < Hp) ? load_elem(Wg + (int64_t)(k0 + k) * Hp + n0 + n) : 0.f;
+        const int64_t at = BT ? (int64_t)(n0 + n) * Hp + k0 + k : (int64_t)(k0 + k) * Hp + n0 + n;
+        Bs[k][n] = (k0 + k < K && n0 + n < N) ? load_elem(Wg + at) : 0.f;
       }
       __syncthreads();
 #pragma unroll
@@ -357,7 +379,7 @@ __global__ __launch_bounds__(256) void ggemm_generic(const T* __restrict__ Xp, c
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int n = n0 + tx * 4 + j;
-        if (n < Hp) store_elem(Yp + (row0 + m) * Hp + n, acc[i][j]);
+        if (n < N) store_elem(Yp + (row0 + m) * N + n, acc[i][j]);
       }
     }
   }
@@ -373,45 +395,63 @@ extern "C" size_t moonep_group_gemm_workspace_bytes(moonep_dims d) {
   return ggemm_ws_bytes(d);
 }
 
-extern "C" int moonep_group_gemm(moonep_dims d, int32_t H, int32_t Hp, moonep_dtype t, const void* Xp,
-                                 const void* W_home, const void* W_slots, const int32_t* cu_seqlens, void* Yp,
-                                 void* workspace, moonep_stream stream) {
-  if (int rc = check_dims(d, "moonep_group_gemm")) return rc;
-  MOONEP_REQUIRE(t == MOONEP_F32 || t == MOONEP_BF16, "moonep_group_gemm: bad dtype %d", (int)t);
-  MOONEP_REQUIRE(H >= 1 && Hp >= 1, "moonep_group_gemm: H and Hp must be >= 1");
+namespace {
+
+// Shared by the forward GEMM and dgrad: BT selects op(W) = W^T (see ggemm_bf16).
+template <bool BT>
+int group_gemm_launch(const char* name, moonep_dims d, int32_t H, int32_t Hp, moonep_dtype t, const void* A,
+                      const void* W_home, const void* W_slots, const int32_t* cu_seqlens, void* C, void* workspace,
+                      moonep_stream stream) {
+  if (int rc = check_dims(d, name)) return rc;
+  MOONEP_REQUIRE(t == MOONEP_F32 || t == MOONEP_BF16, "%s: bad dtype %d", name, (int)t);
+  MOONEP_REQUIRE(H >= 1 && Hp >= 1, "%s: H and Hp must be >= 1", name);
   if (n_pairs(d) == 0) return MOONEP_OK;
-  MOONEP_REQUIRE(Xp && W_home && cu_seqlens && Yp && workspace, "moonep_group_gemm: null pointer");
-  MOONEP_REQUIRE(d.B == 0 || W_slots, "moonep_group_gemm: W_slots is null with B > 0");
-  MOONEP_REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0,
-                 "moonep_group_gemm: workspace must be 256-byte aligned");
-  MOONEP_REQUIRE(n_groups(d) < (int64_t(1) << 30), "moonep_group_gemm: too many groups");
+  MOONEP_REQUIRE(A && W_home && cu_seqlens && C && workspace, "%s: null pointer", name);
+  MOONEP_REQUIRE(d.B == 0 || W_slots, "%s: W_slots is null with B > 0", name);
+  MOONEP_REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, "%s: workspace must be 256-byte aligned",
+                 name);
+  MOONEP_REQUIRE(n_groups(d) < (int64_t(1) << 30), "%s: too many groups", name);
   hipStream_t s = as_stream(stream);
   clear_stale_error();
   int32_t* t256 = static_cast<int32_t*>(workspace);
   int32_t* t64 = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
                                             align256((size_t)(n_groups(d) + 1) * sizeof(int32_t)));
   hipLaunchKernelGGL(ggemm_tiles, dim3(1), dim3(1024), 0, s, cu_seqlens, d.R, d.E, d.B, t256, t64);
-  MOONEP_LAUNCH_CHECK("moonep_group_gemm/tiles");
+  MOONEP_LAUNCH_CHECK(name);
   const int cus = device_cu_count();
-  const bool mfma = t == MOONEP_BF16 && H % 32 == 0 && Hp % 64 == 0 && aligned16(Xp) &&
-                    aligned16(W_home) && (d.B == 0 || aligned16(W_slots));
+  const int K = BT ? Hp : H, N = BT ? H : Hp;
+  const bool mfma = t == MOONEP_BF16 && K % 32 == 0 && N % 64 == 0 && aligned16(A) && aligned16(W_home) &&
+                    (d.B == 0 || aligned16(W_slots));
+  const int P = d.S * d.K;
   if (mfma) {
-    const auto* x = static_cast<const uint16_t*>(Xp);
-    const auto* wh = static_cast<const uint16_t*>(W_home);
-    const auto* ws = static_cast<const uint16_t*>(W_slots);
-    auto* y = static_cast<uint16_t*>(Yp);
-    const int P = d.S * d.K;
-    hipLaunchKernelGGL(fwd::ggemm_bf16, dim3(cus), dim3(512), 0, s, x, wh, ws, cu_seqlens, t256, y, d.R, d.E, d.B,
-                       P, H, Hp);
+    hipLaunchKernelGGL(fwd::ggemm_bf16<BT>, dim3(cus), dim3(512), 0, s, static_cast<const uint16_t*>(A),
+                       static_cast<const uint16_t*>(W_home), static_cast<const uint16_t*>(W_slots), cu_seqlens, t256,
+                       static_cast<uint16_t*>(C), d.R, d.E, d.B, P, H, Hp);
   } else if (t == MOONEP_BF16) {
-    hipLaunchKernelGGL(ggemm_generic<uint16_t>, dim3(cus * 4), dim3(256), 0, s, static_cast<const uint16_t*>(Xp),
+    hipLaunchKernelGGL((ggemm_generic<uint16_t, BT>), dim3(cus * 4), dim3(256), 0, s, static_cast<const uint16_t*>(A),
                        static_cast<const uint16_t*>(W_home), static_cast<const uint16_t*>(W_slots), cu_seqlens, t64,
-                       static_cast<uint16_t*>(Yp), d.R, d.E, d.B, d.S * d.K, H, Hp);
+                       static_cast<uint16_t*>(C), d.R, d.E, d.B, P, H, Hp);
   } else {
-    hipLaunchKernelGGL(ggemm_generic<float>, dim3(cus * 4), dim3(256), 0, s, static_cast<const float*>(Xp),
+    hipLaunchKernelGGL((ggemm_generic<float, BT>), dim3(cus * 4), dim3(256), 0, s, static_cast<const float*>(A),
                        static_cast<const float*>(W_home), static_cast<const float*>(W_slots), cu_seqlens, t64,
-                       static_cast<float*>(Yp), d.R, d.E, d.B, d.S * d.K, H, Hp);
+                       static_cast<float*>(C), d.R, d.E, d.B, P, H, Hp);
   }
-  MOONEP_LAUNCH_CHECK("moonep_group_gemm");
+  MOONEP_LAUNCH_CHECK(name);
   return MOONEP_OK;
+}
+
+}  // namespace
+
+extern "C" int moonep_group_gemm(moonep_dims d, int32_t H, int32_t Hp, moonep_dtype t, const void* Xp,
+                                 const void* W_home, const void* W_slots, const int32_t* cu_seqlens, void* Yp,
+                                 void* workspace, moonep_stream stream) {
+  return group_gemm_launch<false>("moonep_group_gemm", d, H, Hp, t, Xp, W_home, W_slots, cu_seqlens, Yp, workspace,
+                                  stream);
+}
+
+extern "C" int moonep_group_gemm_dgrad(moonep_dims d, int32_t H, int32_t Hp, moonep_dtype t, const void* dYp,
+                                       const void* W_home, const void* W_slots, const int32_t* cu_seqlens, void* dXp,
+                                       void* workspace, moonep_stream stream) {
+  return group_gemm_launch<true>("moonep_group_gemm_dgrad", d, H, Hp, t, dYp, W_home, W_slots, cu_seqlens, dXp,
+                                 workspace, stream);
 }

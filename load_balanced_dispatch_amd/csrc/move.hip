@@ -111,7 +111,8 @@ struct InVec<4> {  // 4 f32
 
 constexpr int kCombineThreads = 256;
 
-// VEC elements of 16 bytes per thread; ESZ = element bytes of Yp.
+// VEC elements of 16 bytes per thread; ESZ = element bytes of Yp.  With gates == nullptr every
+// gate is 1 (the gradient of dispatch: dX[r,s] = sum_k dXp[dest]); fma(1, y, acc) rounds as y + acc.
 template <int VEC, int ESZ>
 __global__ __launch_bounds__(kCombineThreads) void combine_vec(const char* __restrict__ Yp,
                                                                const int32_t* __restrict__ dest,
@@ -129,7 +130,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_vec(const char* __res
   for (int k = 0; k < K; ++k) {
     const int32_t d = dest[tok * K + k];
     if (d < 0) continue;
-    const float g = gates[tok * K + k];
+    const float g = gates ? gates[tok * K + k] : 1.f;
     float y[VEC];
     InVec<VEC>::load(Yp + ((int64_t)d * D + (int64_t)c * VEC) * ESZ, y);
 #pragma unroll
@@ -163,9 +164,107 @@ __global__ __launch_bounds__(kCombineThreads) void combine_scalar(const T* __res
       y = bf16_to_f32(reinterpret_cast<const uint16_t*>(Yp)[(int64_t)d * D + c]);
     else
       y = reinterpret_cast<const float*>(Yp)[(int64_t)d * D + c];
-    acc = __builtin_fmaf(gates[tok * K + k], y, acc);
+    acc = __builtin_fmaf(gates ? gates[tok * K + k] : 1.f, y, acc);
   }
   out[tok * D + c] = acc;
+}
+
+// ------------------------------------------------------------------ combine backward
+
+__device__ __forceinline__ float wave_sum_f(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+template <int ESZ>
+__device__ __forceinline__ void store_scaled(char* p, float g, const float* o);
+template <>
+__device__ __forceinline__ void store_scaled<2>(char* p, float g, const float* o) {  // 8 bf16, rounded to nearest even
+  u32x4 q;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    q[i] = (uint32_t)f32_to_bf16(g * o[2 * i]) | ((uint32_t)f32_to_bf16(g * o[2 * i + 1]) << 16);
+  *reinterpret_cast<u32x4*>(p) = q;
+}
+template <>
+__device__ __forceinline__ void store_scaled<4>(char* p, float g, const float* o) {  // 4 f32
+  *reinterpret_cast<f32x4*>(p) = f32x4{g * o[0], g * o[1], g * o[2], g * o[3]};
+}
+
+// One wave per token; lane c handles 16-byte chunks c, c+64, ... of the Yp row (VEC elements of
+// ESZ bytes).  For each k in ascending order: dYp[dest] = gate * dout (rounded to Yp's type), and
+// dgate = <dout, Yp[dest]> as a float32 FMA chain per lane followed by a fixed butterfly across the
+// wave, so the result does not depend on timing.
+template <int VEC, int ESZ>
+__global__ __launch_bounds__(256) void combine_bwd_vec(const float* __restrict__ dout, const char* __restrict__ Yp,
+                                                       const int32_t* __restrict__ dest,
+                                                       const float* __restrict__ gates, char* __restrict__ dYp,
+                                                       float* __restrict__ dgates, int64_t tokens, int K, int D) {
+  const int lane = threadIdx.x & 63;
+  const int64_t tok = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (tok >= tokens) return;
+  const int nchunk = D / VEC;
+  const float* drow = dout + tok * D;
+  for (int k = 0; k < K; ++k) {
+    const int32_t d = dest[tok * K + k];
+    const float g = gates[tok * K + k];
+    float part = 0.f;
+    if (d >= 0) {
+      for (int c = lane; c < nchunk; c += 64) {
+        float o[VEC], y[VEC];
+#pragma unroll
+        for (int h = 0; h < VEC / 4; ++h) {
+          const f32x4 q = *reinterpret_cast<const f32x4*>(drow + c * VEC + 4 * h);
+          o[4 * h] = q[0];
+          o[4 * h + 1] = q[1];
+          o[4 * h + 2] = q[2];
+          o[4 * h + 3] = q[3];
+        }
+        const int64_t at = ((int64_t)d * D + (int64_t)c * VEC) * ESZ;
+        InVec<VEC>::load(Yp + at, y);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) part = __builtin_fmaf(o[i], y[i], part);
+        store_scaled<ESZ>(dYp + at, g, o);
+      }
+    }
+    part = wave_sum_f(part);
+    if (lane == 0) dgates[tok * K + k] = part;
+  }
+}
+
+// Scalar fallback (rows that are not a whole number of 16-byte chunks): same order of work.
+template <typename T>
+__global__ __launch_bounds__(256) void combine_bwd_scalar(const float* __restrict__ dout, const T* __restrict__ Yp,
+                                                          const int32_t* __restrict__ dest,
+                                                          const float* __restrict__ gates, T* __restrict__ dYp,
+                                                          float* __restrict__ dgates, int64_t tokens, int K, int D) {
+  const int lane = threadIdx.x & 63;
+  const int64_t tok = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (tok >= tokens) return;
+  const float* drow = dout + tok * D;
+  for (int k = 0; k < K; ++k) {
+    const int32_t d = dest[tok * K + k];
+    const float g = gates[tok * K + k];
+    float part = 0.f;
+    if (d >= 0) {
+      for (int c = lane; c < D; c += 64) {
+        const float o = drow[c];
+        const int64_t at = (int64_t)d * D + c;
+        float y;
+        if constexpr (sizeof(T) == 2) {
+          y = bf16_to_f32(Yp[at]);
+          dYp[at] = f32_to_bf16(g * o);
+        } else {
+          y = Yp[at];
+          dYp[at] = g * o;
+        }
+        part = __builtin_fmaf(o, y, part);
+      }
+    }
+    part = wave_sum_f(part);
+    if (lane == 0) dgates[tok * K + k] = part;
+  }
 }
 
 // ------------------------------------------------------------------ reduce_grad
@@ -344,15 +443,12 @@ extern "C" int moonep_prefetch(moonep_dims d, int32_t H, int32_t Hp, moonep_dtyp
   return MOONEP_OK;
 }
 
-extern "C" int moonep_combine(moonep_dims d, int32_t D, moonep_dtype t, const void* Yp, const int32_t* dest_idx,
-                              const float* gates, float* out, moonep_stream stream) {
-  if (int rc = check_dims(d, "moonep_combine")) return rc;
-  MOONEP_REQUIRE(t == MOONEP_F32 || t == MOONEP_BF16, "moonep_combine: bad dtype %d", (int)t);
-  MOONEP_REQUIRE(D >= 1, "moonep_combine: D must be >= 1");
+namespace {
+
+// combine and dispatch backward (gates == nullptr: unit gates)
+int combine_launch(const char* name, moonep_dims d, int32_t D, moonep_dtype t, const void* Yp,
+                   const int32_t* dest_idx, const float* gates, float* out, hipStream_t s) {
   const int64_t tokens = (int64_t)d.R * d.S;
-  if (tokens == 0) return MOONEP_OK;
-  MOONEP_REQUIRE(Yp && dest_idx && gates && out, "moonep_combine: null pointer");
-  hipStream_t s = as_stream(stream);
   clear_stale_error();
   const int vec = t == MOONEP_BF16 ? 8 : 4;
   if (D % vec == 0 && aligned16(Yp) && aligned16(out)) {
@@ -372,8 +468,21 @@ extern "C" int moonep_combine(moonep_dims d, int32_t D, moonep_dtype t, const vo
       hipLaunchKernelGGL(combine_scalar<float>, dim3(grid), dim3(kCombineThreads), 0, s,
                          static_cast<const float*>(Yp), dest_idx, gates, out, tokens, d.K, (int)D);
   }
-  MOONEP_LAUNCH_CHECK("moonep_combine");
+  MOONEP_LAUNCH_CHECK(name);
   return MOONEP_OK;
+}
+
+}  // namespace
+
+extern "C" int moonep_combine(moonep_dims d, int32_t D, moonep_dtype t, const void* Yp, const int32_t* dest_idx,
+                              const float* gates, float* out, moonep_stream stream) {
+  if (int rc = check_dims(d, "moonep_combine")) return rc;
+  MOONEP_REQUIRE(t == MOONEP_F32 || t == MOONEP_BF16, "moonep_combine: bad dtype %d", (int)t);
+  MOONEP_REQUIRE(D >= 1, "moonep_combine: D must be >= 1");
+  const int64_t tokens = (int64_t)d.R * d.S;
+  if (tokens == 0) return MOONEP_OK;
+  MOONEP_REQUIRE(Yp && dest_idx && gates && out, "moonep_combine: null pointer");
+  return combine_launch("moonep_combine", d, D, t, Yp, dest_idx, gates, out, as_stream(stream));
 }
 
 extern "C" int moonep_reduce_grad(moonep_dims d, int32_t H, int32_t Hp, const int32_t* slot_expert, float* dW_home,
@@ -398,4 +507,47 @@ extern "C" int moonep_reduce_grad(moonep_dims d, int32_t H, int32_t Hp, const in
   }
   MOONEP_LAUNCH_CHECK("moonep_reduce_grad");
   return MOONEP_OK;
+}
+
+extern "C" int moonep_combine_backward(moonep_dims d, int32_t D, moonep_dtype t, const float* dout, const void* Yp,
+                                       const int32_t* dest_idx, const float* gates, void* dYp, float* dgates,
+                                       moonep_stream stream) {
+  if (int rc = check_dims(d, "moonep_combine_backward")) return rc;
+  MOONEP_REQUIRE(t == MOONEP_F32 || t == MOONEP_BF16, "moonep_combine_backward: bad dtype %d", (int)t);
+  MOONEP_REQUIRE(D >= 1, "moonep_combine_backward: D must be >= 1");
+  const int64_t tokens = (int64_t)d.R * d.S;
+  if (tokens == 0) return MOONEP_OK;
+  MOONEP_REQUIRE(dout && Yp && dest_idx && gates && dYp && dgates, "moonep_combine_backward: null pointer");
+  hipStream_t s = as_stream(stream);
+  clear_stale_error();
+  const unsigned grid = ceil_div_u(tokens, 4);
+  const int vec = t == MOONEP_BF16 ? 8 : 4;
+  if (D % vec == 0 && aligned16(dout) && aligned16(Yp) && aligned16(dYp)) {
+    if (t == MOONEP_BF16)
+      hipLaunchKernelGGL((combine_bwd_vec<8, 2>), dim3(grid), dim3(256), 0, s, dout, static_cast<const char*>(Yp),
+                         dest_idx, gates, static_cast<char*>(dYp), dgates, tokens, d.K, (int)D);
+    else
+      hipLaunchKernelGGL((combine_bwd_vec<4, 4>), dim3(grid), dim3(256), 0, s, dout, static_cast<const char*>(Yp),
+                         dest_idx, gates, static_cast<char*>(dYp), dgates, tokens, d.K, (int)D);
+  } else if (t == MOONEP_BF16) {
+    hipLaunchKernelGGL(combine_bwd_scalar<uint16_t>, dim3(grid), dim3(256), 0, s, dout,
+                       static_cast<const uint16_t*>(Yp), dest_idx, gates, static_cast<uint16_t*>(dYp), dgates, tokens,
+                       d.K, (int)D);
+  } else {
+    hipLaunchKernelGGL(combine_bwd_scalar<float>, dim3(grid), dim3(256), 0, s, dout, static_cast<const float*>(Yp),
+                       dest_idx, gates, static_cast<float*>(dYp), dgates, tokens, d.K, (int)D);
+  }
+  MOONEP_LAUNCH_CHECK("moonep_combine_backward");
+  return MOONEP_OK;
+}
+
+extern "C" int moonep_dispatch_backward(moonep_dims d, int32_t H, moonep_dtype t, const void* dXp,
+                                        const int32_t* dest_idx, float* dX, moonep_stream stream) {
+  if (int rc = check_dims(d, "moonep_dispatch_backward")) return rc;
+  MOONEP_REQUIRE(t == MOONEP_F32 || t == MOONEP_BF16, "moonep_dispatch_backward: bad dtype %d", (int)t);
+  MOONEP_REQUIRE(H >= 1, "moonep_dispatch_backward: H must be >= 1");
+  const int64_t tokens = (int64_t)d.R * d.S;
+  if (tokens == 0) return MOONEP_OK;
+  MOONEP_REQUIRE(dXp && dest_idx && dX, "moonep_dispatch_backward: null pointer");
+  return combine_launch("moonep_dispatch_backward", d, H, t, dXp, dest_idx, nullptr, dX, as_stream(stream));
 }

@@ -3,9 +3,11 @@
 Every buffer is allocated once, with shapes fixed by (R, E, B, S, K, H, Hp):
 nothing depends on the routing, so repeated passes allocate nothing and a
 pass can be captured in a HIP graph.  The forward pass is
-plan -> dispatch -> prefetch -> group GEMM -> combine; the backward pass is
-wgrad -> reduce_grad.  Each step is one C-ABI call whose kernels do all the
-work; this class only owns memory and passes pointers.
+plan -> dispatch -> prefetch -> group GEMM -> combine; the weight backward is
+wgrad -> reduce_grad; with data_grad=True the data backward is
+combine_backward (writes dY and dgates from dout) -> dgrad -> dispatch_backward
+(dX).  Each step is one C-ABI call whose kernels do all the work; this class
+only owns memory and passes pointers.
 """
 from __future__ import annotations
 
@@ -17,7 +19,7 @@ from ._lib import Dims, make_dims
 
 class MoeLayer:
     def __init__(self, R, E, B, S, K, H, Hp=None, dtype=torch.bfloat16, device="cuda", backward=False,
-                 src_of_row=True):
+                 src_of_row=True, data_grad=False):
         self.d: Dims = make_dims(R, E, B, S, K)
         d = self.d
         self.H, self.Hp, self.dtype, self.device = H, Hp, dtype, device
@@ -51,6 +53,11 @@ class MoeLayer:
                 self.dW_slots = torch.zeros((R, B, H, Hp), dtype=torch.float32, device=device)
                 self.ws_wgrad = torch.empty(max(1, _lib.moonep_wgrad_workspace_bytes(d)), dtype=torch.uint8,
                                             device=device)
+                if data_grad:
+                    self.dout = torch.zeros((R, S, Hp), dtype=torch.float32, device=device)
+                    self.dgates = torch.zeros((R, S, K), dtype=torch.float32, device=device)
+                    self.dXp = torch.empty((N, H), dtype=dtype, device=device)
+                    self.dX = torch.empty((R, S, H), dtype=torch.float32, device=device)
 
     # ---------------------------------------------------------------- steps
     def plan(self, stream=None):
@@ -79,6 +86,23 @@ class MoeLayer:
     def reduce_grad(self, stream=None):
         _lib.moonep_reduce_grad(self.d, self.H, self.Hp, self.slot_expert if self.d.B > 0 else None, self.dW_home,
                                 self.dW_slots if self.d.B > 0 else None, stream)
+
+    def combine_backward(self, stream=None):
+        _lib.moonep_combine_backward(self.d, self.Hp, self.dout, self.Yp, self.dest_idx, self.gates, self.dY,
+                                     self.dgates, stream)
+
+    def dgrad(self, stream=None):
+        _lib.moonep_group_gemm_dgrad(self.d, self.H, self.Hp, self.dY, self.W_home,
+                                     self.W_slots if self.d.B > 0 else None, self.cu_seqlens, self.dXp, self.ws_gemm,
+                                     stream)
+
+    def dispatch_backward(self, stream=None):
+        _lib.moonep_dispatch_backward(self.d, self.H, self.dXp, self.dest_idx, self.dX, stream)
+
+    def backward_data(self, stream=None):
+        self.combine_backward(stream)
+        self.dgrad(stream)
+        self.dispatch_backward(stream)
 
     def forward(self, stream=None):
         self.plan(stream)

@@ -17,10 +17,11 @@ def declared_symbols():
     return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(moonep_\w+)\s*\(", text, flags=re.M)))
 
 
-def test_header_declares_the_seven_calls():
+def test_header_declares_the_calls():
     syms = declared_symbols()
     for name in ("moonep_plan", "moonep_dispatch", "moonep_prefetch", "moonep_group_gemm", "moonep_combine",
-                 "moonep_wgrad", "moonep_reduce_grad"):
+                 "moonep_wgrad", "moonep_reduce_grad", "moonep_combine_backward", "moonep_group_gemm_dgrad",
+                 "moonep_dispatch_backward"):
         assert name in syms
 
 
@@ -59,6 +60,9 @@ def test_bad_dims_rejected_everywhere(dims, msg):
         lambda: L.moonep_combine(d, 8, 1, null, null, null, null, null),
         lambda: L.moonep_wgrad(d, 8, 8, 1, *([null] * 7)),
         lambda: L.moonep_reduce_grad(d, 8, 8, null, null, null, null),
+        lambda: L.moonep_combine_backward(d, 8, 1, *([null] * 7)),
+        lambda: L.moonep_group_gemm_dgrad(d, 8, 8, 1, *([null] * 7)),
+        lambda: L.moonep_dispatch_backward(d, 8, 1, null, null, null, null),
     ]
     for c in calls:
         assert c() == _lib.MOONEP_EINVAL
@@ -76,12 +80,19 @@ def test_null_pointers_rejected():
     assert L.moonep_group_gemm(d, 8, 8, 1, *([None] * 7)) == _lib.MOONEP_EINVAL
     assert L.moonep_wgrad(d, 8, 8, 1, *([None] * 7)) == _lib.MOONEP_EINVAL
     assert L.moonep_reduce_grad(d, 8, 8, None, None, None, None) == _lib.MOONEP_EINVAL
+    assert L.moonep_combine_backward(d, 8, 1, *([None] * 7)) == _lib.MOONEP_EINVAL
+    assert L.moonep_group_gemm_dgrad(d, 8, 8, 1, *([None] * 7)) == _lib.MOONEP_EINVAL
+    assert L.moonep_dispatch_backward(d, 8, 1, None, None, None, None) == _lib.MOONEP_EINVAL
 
 
 def test_bad_dtype_rejected():
     d = m.make_dims(2, 4, 1, 3, 1)
     L = _lib.lib()
     assert L.moonep_dispatch(d, 8, 7, None, None, None, None) == _lib.MOONEP_EINVAL
+    assert "dtype" in m.last_error()
+    assert L.moonep_combine_backward(d, 8, 7, *([None] * 7)) == _lib.MOONEP_EINVAL
+    assert "dtype" in m.last_error()
+    assert L.moonep_group_gemm_dgrad(d, 8, 8, 7, *([None] * 7)) == _lib.MOONEP_EINVAL
     assert "dtype" in m.last_error()
 
 
@@ -93,6 +104,9 @@ def test_empty_work_is_a_no_op():
     assert L.moonep_combine(d, 8, 1, None, None, None, None, None) == _lib.MOONEP_OK
     assert L.moonep_group_gemm(d, 8, 8, 1, *([None] * 7)) == _lib.MOONEP_OK
     assert L.moonep_wgrad(d, 8, 8, 1, *([None] * 7)) == _lib.MOONEP_OK
+    assert L.moonep_combine_backward(d, 8, 1, *([None] * 7)) == _lib.MOONEP_OK
+    assert L.moonep_group_gemm_dgrad(d, 8, 8, 1, *([None] * 7)) == _lib.MOONEP_OK
+    assert L.moonep_dispatch_backward(d, 8, 1, None, None, None, None) == _lib.MOONEP_OK
 
 
 def test_binding_refuses_host_tensors():
