@@ -11,8 +11,12 @@ Default workload: R8 E64 K6 S4096 H2048 H'1408 B8 (bf16 activations and
 weights, fp32 gradients), routing skew calibrated to maxvio ~ 1; the sweep adds
 maxvio ~ 0, 2, 3.  value = token-expert pairs per second through the whole
 step; the JSON also carries plan+dispatch pairs/s, group-GEMM TFLOP/s and
-reduce_grad GB/s, the dominant kernel's roofline and the CPU oracle's rate on
-a bounded sample.
+reduce_grad GB/s, every stage's roofline (the longest stage's as `roofline`),
+the backward of the data path (combine backward, dgrad, dispatch backward) timed
+after the step as `next_rows`, and the CPU oracle's rate on a bounded sample.
+
+    python bench.py --stats-md run_kernel_stats.csv          (rocprofv3 summary -> markdown)
+    python bench.py --traffic-md fetch.csv write.csv         (counter runs -> per-stage HBM bytes)
 """
 from __future__ import annotations
 
@@ -68,7 +72,7 @@ def make_layer(wl, backward):
     import load_balanced_dispatch_amd as m
     dt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
     return m.MoeLayer(wl.R, wl.E, wl.B, wl.S, wl.K, wl.H, wl.Hp, dtype=dt, device="cuda", backward=backward,
-                      src_of_row=False)
+                      src_of_row=False, data_grad=backward)
 
 
 def load_inputs(L, wl, seed, alpha):
@@ -127,6 +131,34 @@ def time_steps(L, backward, steps, warmup):
     return (t1 - t0) * 1e3 / steps, stages
 
 
+def next_calls(L):
+    return [("combine_backward", L.combine_backward), ("dgrad", L.dgrad), ("dispatch_backward", L.dispatch_backward)]
+
+
+def time_next_rows(L, steps, warmup):
+    """The backward of the data path (combine backward -> dgrad -> dispatch backward) on the same
+    workload: dout ~ N(0, 1) drawn once on the device, a forward pass for Yp, then K timed passes with
+    HIP events between the calls, as for the step."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(7)
+    L.dout.normal_(generator=g)
+    L.forward()
+    calls = next_calls(L)
+    for _ in range(warmup):
+        for _, f in calls:
+            f()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(steps)]
+    for s in range(steps):
+        evs[s][0].record()
+        for i, (_, f) in enumerate(calls):
+            f()
+            evs[s][i + 1].record()
+    torch.cuda.synchronize()
+    return {n: sum(evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(steps)) / steps
+            for i, (n, _) in enumerate(calls)}
+
+
 def algorithmic(wl, stats, slot_expert_np, L):
     """Algorithmic work per launch of each stage: bytes for the bandwidth-bound stages (every input byte
     read once, every output byte written once), flops for the two GEMMs plus the least HBM bytes they can
@@ -150,35 +182,61 @@ def algorithmic(wl, stats, slot_expert_np, L):
         out["reduce_grad"] = 4 * H * Hp * (2 * len(np.unique(used)) + 2 * len(used))
         out["wgrad"] = 2 * N * H * Hp
         out["wgrad_min_bytes"] = N * (H + Hp) * b + 8 * H * Hp * (home_used + slots_used)
+        # backward of the data path
+        out["combine_backward"] = T * Hp * 4 + 2 * N * Hp * b + 12 * N
+        out["dgrad"] = 2 * N * H * Hp
+        out["dgrad_min_bytes"] = N * Hp * b + (home_used + slots_used) * H * Hp * b + N * H * b
+        out["dispatch_backward"] = N * H * b + T * H * 4 + 4 * N
     return out
 
 
-# library kernels of each stage (rocprofv3 base names) and the source file that holds them
+# library kernels of each stage, matched on "base<template args>" names, and the source file that holds them
 STAGE_KERNELS = {
-    "plan": ("plan_count", "plan_scan", "plan_solve", "plan_emit"),
-    "dispatch": ("dispatch_rows",),
-    "prefetch": ("prefetch_slots",),
-    "group_gemm": ("ggemm_tiles", "ggemm_bf16", "ggemm_generic"),
-    "combine": ("combine_vec", "combine_scalar"),
-    "wgrad": ("wgrad_schedule", "wgrad_bf16", "wgrad_generic"),
-    "reduce_grad": ("reduce_grad_kernel", "reduce_grad_scalar"),
+    "plan": r"^plan_(count|scan|solve|emit)$",
+    "dispatch": r"^dispatch_rows<",
+    "prefetch": r"^prefetch_slots<",
+    "group_gemm": r"^(ggemm_tiles$|ggemm_bf16<false>|ggemm_generic<.*false>)",
+    "combine": r"^combine_(vec|scalar)<.*true>",
+    "wgrad": r"^wgrad_(schedule|bf16|generic)",
+    "reduce_grad": r"^reduce_grad_(kernel|scalar)",
+    "combine_backward": r"^combine_bwd_",
+    "dgrad": r"^(ggemm_bf16<true>|ggemm_generic<.*true>)",
+    "dispatch_backward": r"^combine_(vec|scalar)<.*false>",
 }
 STAGE_SOURCE = {"plan": "plan.hip", "dispatch": "move.hip", "prefetch": "move.hip", "group_gemm": "ggemm.hip",
-                "combine": "move.hip", "wgrad": "wgrad.hip", "reduce_grad": "move.hip"}
+                "combine": "move.hip", "wgrad": "wgrad.hip", "reduce_grad": "move.hip",
+                "combine_backward": "move.hip", "dgrad": "ggemm.hip", "dispatch_backward": "move.hip"}
+GEMM_STAGES = ("group_gemm", "wgrad", "dgrad")
+NEXT_STAGES = ("combine_backward", "dgrad", "dispatch_backward")
 CSRC = os.path.join(ROOT, "load_balanced_dispatch_amd", "csrc")
 
 
 def kernel_base(name):
-    """Base identifier of a demangled kernel name as rocprofv3 prints it."""
+    """'base<template args>' of a demangled kernel name as rocprofv3 prints it (args kept: they tell
+    instantiations such as the forward and dgrad GEMMs apart)."""
     n = name.replace("(anonymous namespace)::", "")
     if n.startswith("void "):
         n = n[5:]
-    return re.split(r"[<(]", n, maxsplit=1)[0].rsplit("::", 1)[-1]
+    cut = len(n)
+    for i, ch in enumerate(n):
+        if ch in "<(":
+            cut = i
+            break
+    base = n[:cut].rsplit("::", 1)[-1]
+    if cut < len(n) and n[cut] == "<":
+        depth, j = 0, cut
+        while j < len(n):
+            depth += (n[j] == "<") - (n[j] == ">")
+            j += 1
+            if depth == 0:
+                break
+        base += n[cut:j]
+    return base
 
 
 def stage_of(base):
-    for st, ks in STAGE_KERNELS.items():
-        if base in ks:
+    for st, pat in STAGE_KERNELS.items():
+        if re.search(pat, base):
             return st
     return None
 
@@ -215,7 +273,7 @@ def load_traffic(wl, target):
 
 
 def stage_roofline(name, alg, ms, traffic, f32):
-    gemm = name in ("group_gemm", "wgrad")
+    gemm = name in GEMM_STAGES
     if gemm:
         bound, unit = ("alu", "TFLOP/s") if f32 else ("mfma", "TFLOP/s")
         peak = MFMA_F32_VECTOR_TFLOPS if f32 else MFMA_BF16_PEAK_TFLOPS
@@ -272,8 +330,8 @@ def traffic_markdown(fetch_csv, write_csv, wl, target):
     stages = {}
     lines = ["| stage | kernels | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes per launch (scaled) |",
              "|---|---|---|---|---|---|"]
-    for st, ks in STAGE_KERNELS.items():
-        ks = [k for k in ks if k in fetch and k in write]
+    for st in STAGE_KERNELS:
+        ks = sorted(k for k in fetch if stage_of(k) == st and k in write)
         if not ks:
             continue
         f = sum(fetch[k] for k in ks)
@@ -377,8 +435,10 @@ def main():
     L = make_layer(wl, backward)
     if args.profile_pass:
         load_inputs(L, wl, args.seed, alpha_of(head_target))
+        if backward:
+            L.dout.normal_()
         for _ in range(1 + args.steps):
-            for _, f in stage_calls(L, backward):
+            for _, f in stage_calls(L, backward) + (next_calls(L) if backward else []):
                 f()
         torch.cuda.synchronize()
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -418,6 +478,12 @@ def main():
                                        if alg["reduce_grad"] else None)
     traffic = load_traffic(wl, head_target)
     rooflines = {n: stage_roofline(n, alg, st[n], traffic, wl.dtype == "f32") for n in st}
+    next_rows = None
+    if backward:
+        load_inputs(L, wl, args.seed, h["alpha"])  # the headline routing again (the sweep moved it)
+        nx = time_next_rows(L, args.steps, args.warmup)
+        log(f"backward of the data path: {nx}")
+        next_rows = {n: stage_roofline(n, alg, nx[n], traffic, wl.dtype == "f32") for n in nx}
     dominant = max(st, key=lambda n: st[n])
     roofline = dict(rooflines[dominant], stage=dominant)
 
@@ -451,6 +517,7 @@ def main():
         "components": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in comp.items()},
         "roofline": roofline,
         "rooflines": rooflines,
+        "next_rows": next_rows,
         "cpu_baseline": cpu,
         "sweep": sweep,
     }

@@ -111,9 +111,10 @@ struct InVec<4> {  // 4 f32
 
 constexpr int kCombineThreads = 256;
 
-// VEC elements of 16 bytes per thread; ESZ = element bytes of Yp.  With gates == nullptr every
-// gate is 1 (the gradient of dispatch: dX[r,s] = sum_k dXp[dest]); fma(1, y, acc) rounds as y + acc.
-template <int VEC, int ESZ>
+// VEC elements of 16 bytes per thread; ESZ = element bytes of Yp.  With GATED false every gate is 1
+// and gates is not read (the gradient of dispatch: dX[r,s] = sum_k dXp[dest]); fma(1, y, acc)
+// rounds as y + acc.
+template <int VEC, int ESZ, bool GATED>
 __global__ __launch_bounds__(kCombineThreads) void combine_vec(const char* __restrict__ Yp,
                                                                const int32_t* __restrict__ dest,
                                                                const float* __restrict__ gates,
@@ -130,7 +131,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_vec(const char* __res
   for (int k = 0; k < K; ++k) {
     const int32_t d = dest[tok * K + k];
     if (d < 0) continue;
-    const float g = gates ? gates[tok * K + k] : 1.f;
+    const float g = GATED ? gates[tok * K + k] : 1.f;
     float y[VEC];
     InVec<VEC>::load(Yp + ((int64_t)d * D + (int64_t)c * VEC) * ESZ, y);
 #pragma unroll
@@ -145,7 +146,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_vec(const char* __res
 }
 
 // Scalar fallback for widths that are not a multiple of 16 bytes.
-template <typename T>
+template <typename T, bool GATED>
 __global__ __launch_bounds__(kCombineThreads) void combine_scalar(const T* __restrict__ Yp,
                                                                   const int32_t* __restrict__ dest,
                                                                   const float* __restrict__ gates,
@@ -164,7 +165,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_scalar(const T* __res
       y = bf16_to_f32(reinterpret_cast<const uint16_t*>(Yp)[(int64_t)d * D + c]);
     else
       y = reinterpret_cast<const float*>(Yp)[(int64_t)d * D + c];
-    acc = __builtin_fmaf(gates ? gates[tok * K + k] : 1.f, y, acc);
+    acc = __builtin_fmaf(GATED ? gates[tok * K + k] : 1.f, y, acc);
   }
   out[tok * D + c] = acc;
 }
@@ -193,10 +194,12 @@ __device__ __forceinline__ void store_scaled<4>(char* p, float g, const float* o
 }
 
 // One wave per token; lane c handles 16-byte chunks c, c+64, ... of the Yp row (VEC elements of
-// ESZ bytes).  For each k in ascending order: dYp[dest] = gate * dout (rounded to Yp's type), and
-// dgate = <dout, Yp[dest]> as a float32 FMA chain per lane followed by a fixed butterfly across the
-// wave, so the result does not depend on timing.
-template <int VEC, int ESZ>
+// ESZ bytes).  The lane's part of the dout row is read once into registers (CPL chunks at most;
+// CPL = 0: rows too wide for that, read again for every k).  For each k in ascending order:
+// dYp[dest] = gate * dout (rounded to Yp's type), and dgate = <dout, Yp[dest]> as a float32 FMA
+// chain per lane followed by a fixed butterfly across the wave, so the result does not depend on
+// timing.
+template <int VEC, int ESZ, int CPL>
 __global__ __launch_bounds__(256) void combine_bwd_vec(const float* __restrict__ dout, const char* __restrict__ Yp,
                                                        const int32_t* __restrict__ dest,
                                                        const float* __restrict__ gates, char* __restrict__ dYp,
@@ -206,26 +209,46 @@ __global__ __launch_bounds__(256) void combine_bwd_vec(const float* __restrict__
   if (tok >= tokens) return;
   const int nchunk = D / VEC;
   const float* drow = dout + tok * D;
+  auto load_dout = [&](int c, float (&o)[VEC]) {
+#pragma unroll
+    for (int h = 0; h < VEC / 4; ++h) {
+      const f32x4 q = *reinterpret_cast<const f32x4*>(drow + c * VEC + 4 * h);
+      o[4 * h] = q[0];
+      o[4 * h + 1] = q[1];
+      o[4 * h + 2] = q[2];
+      o[4 * h + 3] = q[3];
+    }
+  };
+  constexpr int NR = CPL > 0 ? CPL : 1;
+  float o_reg[NR][VEC];
+  if constexpr (CPL > 0) {
+#pragma unroll
+    for (int i = 0; i < CPL; ++i)
+      if (lane + 64 * i < nchunk) load_dout(lane + 64 * i, o_reg[i]);
+  }
   for (int k = 0; k < K; ++k) {
     const int32_t d = dest[tok * K + k];
     const float g = gates[tok * K + k];
     float part = 0.f;
     if (d >= 0) {
-      for (int c = lane; c < nchunk; c += 64) {
-        float o[VEC], y[VEC];
-#pragma unroll
-        for (int h = 0; h < VEC / 4; ++h) {
-          const f32x4 q = *reinterpret_cast<const f32x4*>(drow + c * VEC + 4 * h);
-          o[4 * h] = q[0];
-          o[4 * h + 1] = q[1];
-          o[4 * h + 2] = q[2];
-          o[4 * h + 3] = q[3];
-        }
+      auto chunk = [&](int c, const float (&o)[VEC]) {
+        float y[VEC];
         const int64_t at = ((int64_t)d * D + (int64_t)c * VEC) * ESZ;
         InVec<VEC>::load(Yp + at, y);
 #pragma unroll
         for (int i = 0; i < VEC; ++i) part = __builtin_fmaf(o[i], y[i], part);
         store_scaled<ESZ>(dYp + at, g, o);
+      };
+      if constexpr (CPL > 0) {
+#pragma unroll
+        for (int i = 0; i < CPL; ++i)
+          if (lane + 64 * i < nchunk) chunk(lane + 64 * i, o_reg[i]);
+      } else {
+        for (int c = lane; c < nchunk; c += 64) {
+          float o[VEC];
+          load_dout(c, o);
+          chunk(c, o);
+        }
       }
     }
     part = wave_sum_f(part);
@@ -445,7 +468,8 @@ extern "C" int moonep_prefetch(moonep_dims d, int32_t H, int32_t Hp, moonep_dtyp
 
 namespace {
 
-// combine and dispatch backward (gates == nullptr: unit gates)
+// combine (GATED) and dispatch backward (unit gates)
+template <bool GATED>
 int combine_launch(const char* name, moonep_dims d, int32_t D, moonep_dtype t, const void* Yp,
                    const int32_t* dest_idx, const float* gates, float* out, hipStream_t s) {
   const int64_t tokens = (int64_t)d.R * d.S;
@@ -454,18 +478,18 @@ int combine_launch(const char* name, moonep_dims d, int32_t D, moonep_dtype t, c
   if (D % vec == 0 && aligned16(Yp) && aligned16(out)) {
     const unsigned grid = ceil_div_u(tokens * (D / vec), kCombineThreads);
     if (t == MOONEP_BF16)
-      hipLaunchKernelGGL((combine_vec<8, 2>), dim3(grid), dim3(kCombineThreads), 0, s,
+      hipLaunchKernelGGL((combine_vec<8, 2, GATED>), dim3(grid), dim3(kCombineThreads), 0, s,
                          static_cast<const char*>(Yp), dest_idx, gates, out, tokens, d.K, (int)D);
     else
-      hipLaunchKernelGGL((combine_vec<4, 4>), dim3(grid), dim3(kCombineThreads), 0, s,
+      hipLaunchKernelGGL((combine_vec<4, 4, GATED>), dim3(grid), dim3(kCombineThreads), 0, s,
                          static_cast<const char*>(Yp), dest_idx, gates, out, tokens, d.K, (int)D);
   } else {
     const unsigned grid = ceil_div_u(tokens * D, kCombineThreads);
     if (t == MOONEP_BF16)
-      hipLaunchKernelGGL(combine_scalar<uint16_t>, dim3(grid), dim3(kCombineThreads), 0, s,
+      hipLaunchKernelGGL((combine_scalar<uint16_t, GATED>), dim3(grid), dim3(kCombineThreads), 0, s,
                          static_cast<const uint16_t*>(Yp), dest_idx, gates, out, tokens, d.K, (int)D);
     else
-      hipLaunchKernelGGL(combine_scalar<float>, dim3(grid), dim3(kCombineThreads), 0, s,
+      hipLaunchKernelGGL((combine_scalar<float, GATED>), dim3(grid), dim3(kCombineThreads), 0, s,
                          static_cast<const float*>(Yp), dest_idx, gates, out, tokens, d.K, (int)D);
   }
   MOONEP_LAUNCH_CHECK(name);
@@ -482,7 +506,7 @@ extern "C" int moonep_combine(moonep_dims d, int32_t D, moonep_dtype t, const vo
   const int64_t tokens = (int64_t)d.R * d.S;
   if (tokens == 0) return MOONEP_OK;
   MOONEP_REQUIRE(Yp && dest_idx && gates && out, "moonep_combine: null pointer");
-  return combine_launch("moonep_combine", d, D, t, Yp, dest_idx, gates, out, as_stream(stream));
+  return combine_launch<true>("moonep_combine", d, D, t, Yp, dest_idx, gates, out, as_stream(stream));
 }
 
 extern "C" int moonep_reduce_grad(moonep_dims d, int32_t H, int32_t Hp, const int32_t* slot_expert, float* dW_home,
@@ -523,12 +547,24 @@ extern "C" int moonep_combine_backward(moonep_dims d, int32_t D, moonep_dtype t,
   const unsigned grid = ceil_div_u(tokens, 4);
   const int vec = t == MOONEP_BF16 ? 8 : 4;
   if (D % vec == 0 && aligned16(dout) && aligned16(Yp) && aligned16(dYp)) {
-    if (t == MOONEP_BF16)
-      hipLaunchKernelGGL((combine_bwd_vec<8, 2>), dim3(grid), dim3(256), 0, s, dout, static_cast<const char*>(Yp),
-                         dest_idx, gates, static_cast<char*>(dYp), dgates, tokens, d.K, (int)D);
-    else
-      hipLaunchKernelGGL((combine_bwd_vec<4, 4>), dim3(grid), dim3(256), 0, s, dout, static_cast<const char*>(Yp),
-                         dest_idx, gates, static_cast<char*>(dYp), dgates, tokens, d.K, (int)D);
+    const int cpl = (D / vec + 63) / 64;  // 16-byte chunks per lane
+    const char* y = static_cast<const char*>(Yp);
+    char* dy = static_cast<char*>(dYp);
+#define MOONEP_CBWD(V, ES, C)                                                                                  \
+  hipLaunchKernelGGL((combine_bwd_vec<V, ES, C>), dim3(grid), dim3(256), 0, s, dout, y, dest_idx, gates, dy, dgates, \
+                     tokens, d.K, (int)D)
+    if (t == MOONEP_BF16) {
+      if (cpl <= 1) MOONEP_CBWD(8, 2, 1);
+      else if (cpl == 2) MOONEP_CBWD(8, 2, 2);
+      else if (cpl <= 4) MOONEP_CBWD(8, 2, 4);
+      else MOONEP_CBWD(8, 2, 0);
+    } else {
+      if (cpl <= 1) MOONEP_CBWD(4, 4, 1);
+      else if (cpl == 2) MOONEP_CBWD(4, 4, 2);
+      else if (cpl <= 4) MOONEP_CBWD(4, 4, 4);
+      else MOONEP_CBWD(4, 4, 0);
+    }
+#undef MOONEP_CBWD
   } else if (t == MOONEP_BF16) {
     hipLaunchKernelGGL(combine_bwd_scalar<uint16_t>, dim3(grid), dim3(256), 0, s, dout,
                        static_cast<const uint16_t*>(Yp), dest_idx, gates, static_cast<uint16_t*>(dYp), dgates, tokens,
@@ -549,5 +585,5 @@ extern "C" int moonep_dispatch_backward(moonep_dims d, int32_t H, moonep_dtype t
   const int64_t tokens = (int64_t)d.R * d.S;
   if (tokens == 0) return MOONEP_OK;
   MOONEP_REQUIRE(dXp && dest_idx && dX, "moonep_dispatch_backward: null pointer");
-  return combine_launch("moonep_dispatch_backward", d, H, t, dXp, dest_idx, nullptr, dX, as_stream(stream));
+  return combine_launch<false>("moonep_dispatch_backward", d, H, t, dXp, dest_idx, nullptr, dX, as_stream(stream));
 }

@@ -41,6 +41,7 @@ def scaled_rounded(g: np.ndarray, dout: np.ndarray, dtype) -> torch.Tensor:
 
 
 @pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 1408), (torch.bfloat16, 2048), (torch.float32, 256),
+                                     (torch.bfloat16, 1024), (torch.bfloat16, 4096), (torch.float32, 1000),
                                      (torch.bfloat16, 13), (torch.float32, 6)])
 def test_combine_backward(m, dtype, D):
     rng = np.random.default_rng(100 + D)
