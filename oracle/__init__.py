@@ -20,8 +20,9 @@ Modules:
                step (a heuristic, so the oracle follows its steps).
   layer     -- dispatch, prefetch, group GEMM, combine, wgrad, reduce_grad, the
                backward of the data path (combine backward, group-GEMM dgrad,
-               dispatch backward), and the plain MoE definitions (forward and
-               gradients) they must reproduce.
+               dispatch backward), the gated expert FFN's activation (silu,
+               swiglu and its gradient), and the plain MoE definitions (forward
+               and gradients, single projection and full FFN) they must reproduce.
   mincopies -- brute-force minimum number of redundant copies on tiny inputs.
 
 Parity status: every function here is pinned by a ``-m "not gpu"`` test

@@ -1,4 +1,5 @@
-"""Oracle: the data-moving and arithmetic stages of the layer, forward and backward (test infrastructure).
+"""Oracle: the data-moving and arithmetic stages of the layer, forward and backward, and the full
+gated expert FFN built from them (test infrastructure).
 
 Plain numpy, float64 arithmetic on whatever values the caller passes (the
 tests pass bf16-rounded inputs converted to float64).
@@ -217,6 +218,41 @@ def dispatch_backward(dXp: np.ndarray, dest_idx: np.ndarray, tokens=None) -> np.
     return dX if tokens is not None else dX.reshape(R, S, H)
 
 
+# ------------------------------------------------------------------ full expert FFN
+#
+# The pages call the weight tensor one "expert projection" and ask for one such tensor per
+# projection ([P2] "Memory contract and weight layout"); they do not name the FFN.  Read plainly
+# (the usual gated MoE expert): a gate|up projection [E+B, H, 2H'] whose first H' output columns are
+# the gate and last H' the up projection, act = silu(gate) * up, and a down projection
+# [E+B, H', H]; each projection runs through the same plan, slots and group GEMM.
+
+def silu(g):
+    """g * sigmoid(g), from exp of a non-positive argument only (no overflow)."""
+    g = np.asarray(g, dtype=np.float64)
+    e = np.exp(-np.abs(g))
+    sig = np.where(g >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+    return g * sig
+
+
+def swiglu(Ygu: np.ndarray) -> np.ndarray:
+    """act = silu(gate) * up for rows [gate (H') | up (H')]."""
+    Y = np.asarray(Ygu, dtype=np.float64)
+    Hp = Y.shape[1] // 2
+    return silu(Y[:, :Hp]) * Y[:, Hp:]
+
+
+def swiglu_backward(Ygu: np.ndarray, dA: np.ndarray) -> np.ndarray:
+    """Gradient of swiglu: d gate = dA * up * s * (1 + g * (1 - s)) with s = sigmoid(g), d up = dA * silu(g);
+    returned as rows [d gate | d up]."""
+    Y = np.asarray(Ygu, dtype=np.float64)
+    Hp = Y.shape[1] // 2
+    g, u = Y[:, :Hp], Y[:, Hp:]
+    d = np.asarray(dA, dtype=np.float64)
+    e = np.exp(-np.abs(g))
+    s = np.where(g >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+    return np.concatenate([d * u * s * (1.0 + g * (1.0 - s)), d * g * s], axis=1)
+
+
 # ------------------------------------------------------------------ plain definitions
 
 def moe_forward(X, W_home, topk_idx, gates, tokens=None) -> np.ndarray:
@@ -269,3 +305,20 @@ def moe_backward(X, W_home, topk_idx, gates, dout):
             dX[t] += gf[t, k] * (w @ do[t])
             dgate[t, k] = do[t] @ (Xf[t] @ w)
     return dX.reshape(R, S, H), dgate.reshape(R, S, K)
+
+
+def moe_ffn_forward(X, W_gu, W_down, topk_idx, gates) -> np.ndarray:
+    """Plain gated-expert MoE: out[r,s] = sum_k gate * ffn_e(X[r,s]),
+    ffn_e(x) = swiglu(x @ W_gu[e]) @ W_down[e]."""
+    R, S, H = X.shape
+    K = topk_idx.shape[2]
+    Xf = X.reshape(R * S, H).astype(np.float64)
+    ids = np.asarray(topk_idx).reshape(R * S, K)
+    gf = np.asarray(gates, dtype=np.float64).reshape(R * S, K)
+    out = np.zeros((R * S, W_down.shape[2]), dtype=np.float64)
+    for t in range(R * S):
+        for k in range(K):
+            e = ids[t, k]
+            a = swiglu((Xf[t] @ W_gu[e].astype(np.float64))[None, :])[0]
+            out[t] += gf[t, k] * (a @ W_down[e].astype(np.float64))
+    return out.reshape(R, S, -1)
