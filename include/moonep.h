@@ -206,6 +206,31 @@ int moonep_group_gemm_dgrad(moonep_dims d, int32_t H, int32_t Hp, moonep_dtype t
 int moonep_dispatch_backward(moonep_dims d, int32_t H, moonep_dtype t, const void* dXp, const int32_t* dest_idx,
                              float* dX, moonep_stream stream);
 
+/*
+ * Full gated expert FFN.  The pages ask for one [E+B, H, H'] tensor per expert projection ([P2]
+ * "Memory contract and weight layout") without naming the FFN; read plainly it is the gated expert:
+ * a gate|up projection [E+B, H, 2H'] (gate in output columns [0, H'), up in [H', 2H')), then
+ * act = silu(gate) * up, then a down projection [E+B, H', H].  Both projections run through
+ * moonep_group_gemm / moonep_group_gemm_dgrad / moonep_wgrad / moonep_reduce_grad with their own
+ * (H, Hp) -- (H, 2H') and (H', H) -- and the same plan; these two calls are the activation.
+ */
+
+/*
+ * moonep_swiglu -- A[q, c] = silu(Ygu[q, c]) * Ygu[q, Hp + c] for every dispatched row q < R*S*K and
+ *   c < Hp, silu(g) = g * sigmoid(g); float32 arithmetic, rounded once to dtype t.
+ * In:  Ygu [R*S*K, 2*Hp] dtype t.   Out: A [R*S*K, Hp] dtype t.
+ */
+int moonep_swiglu(moonep_dims d, int32_t Hp, moonep_dtype t, const void* Ygu, void* A, moonep_stream stream);
+
+/*
+ * moonep_swiglu_backward -- gradient of moonep_swiglu: with g = Ygu[q,c], u = Ygu[q,Hp+c],
+ *   s = sigmoid(g), da = dA[q,c]:  dYgu[q,c] = da * u * s * (1 + g * (1 - s)),  dYgu[q,Hp+c] = da * g * s;
+ *   float32 arithmetic, rounded once to dtype t.
+ * In:  Ygu [R*S*K, 2*Hp], dA [R*S*K, Hp] dtype t.   Out: dYgu [R*S*K, 2*Hp] dtype t.
+ */
+int moonep_swiglu_backward(moonep_dims d, int32_t Hp, moonep_dtype t, const void* Ygu, const void* dA, void* dYgu,
+                           moonep_stream stream);
+
 /* Bytes of device workspace moonep_wgrad needs. */
 size_t moonep_wgrad_workspace_bytes(moonep_dims d);
 

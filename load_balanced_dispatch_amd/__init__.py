@@ -2,9 +2,11 @@
 
 The C ABI (include/moonep.h) has the seven calls of the layer -- moonep_plan,
 moonep_dispatch, moonep_prefetch, moonep_group_gemm, moonep_combine,
-moonep_wgrad, moonep_reduce_grad -- and three for the backward of the data path
--- moonep_combine_backward, moonep_group_gemm_dgrad, moonep_dispatch_backward --
-exposed here under the same names, taking torch tensors.  Importing this
+moonep_wgrad, moonep_reduce_grad -- three for the backward of the data path --
+moonep_combine_backward, moonep_group_gemm_dgrad, moonep_dispatch_backward --
+and two for the activation of the gated expert FFN -- moonep_swiglu,
+moonep_swiglu_backward -- exposed here under the same names, taking torch
+tensors.  Importing this
 package loads libmoonep.so and raises if it is missing; there is no CPU or
 PyTorch fallback.
 """
@@ -12,6 +14,8 @@ from ._lib import (  # noqa: F401
     Dims, MoonepError, LIB_PATH, SYMBOLS, MOONEP_F32, MOONEP_BF16, make_dims, last_error,
     moonep_plan_workspace_bytes, moonep_group_gemm_workspace_bytes, moonep_wgrad_workspace_bytes, moonep_plan,
     moonep_dispatch, moonep_prefetch, moonep_group_gemm, moonep_combine, moonep_wgrad, moonep_reduce_grad,
-    moonep_combine_backward, moonep_group_gemm_dgrad, moonep_dispatch_backward,
+    moonep_combine_backward, moonep_group_gemm_dgrad, moonep_dispatch_backward, moonep_swiglu,
+    moonep_swiglu_backward,
 )
+from .layer import MoeFFN  # noqa: F401
 from .layer import MoeLayer  # noqa: F401

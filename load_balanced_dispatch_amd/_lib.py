@@ -68,6 +68,8 @@ def _load():
         "moonep_combine_backward": (ctypes.c_int, [Dims, i32, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp]),
         "moonep_group_gemm_dgrad": (ctypes.c_int, [Dims, i32, i32, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp]),
         "moonep_dispatch_backward": (ctypes.c_int, [Dims, i32, ctypes.c_int, vp, vp, vp, vp]),
+        "moonep_swiglu": (ctypes.c_int, [Dims, i32, ctypes.c_int, vp, vp, vp]),
+        "moonep_swiglu_backward": (ctypes.c_int, [Dims, i32, ctypes.c_int, vp, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -82,7 +84,7 @@ _LIB = _load()
 SYMBOLS = ("moonep_last_error", "moonep_plan_workspace_bytes", "moonep_plan", "moonep_dispatch", "moonep_prefetch",
            "moonep_group_gemm_workspace_bytes", "moonep_group_gemm", "moonep_combine",
            "moonep_wgrad_workspace_bytes", "moonep_wgrad", "moonep_reduce_grad", "moonep_combine_backward",
-           "moonep_group_gemm_dgrad", "moonep_dispatch_backward")
+           "moonep_group_gemm_dgrad", "moonep_dispatch_backward", "moonep_swiglu", "moonep_swiglu_backward")
 
 
 def lib():
@@ -264,3 +266,16 @@ def moonep_dispatch_backward(d: Dims, H: int, dXp, dest_idx, dX, stream=None):
     _check(_LIB.moonep_dispatch_backward(d, int(H), t, _ptr(dXp, "dXp", dXp.dtype, d.N * H),
                                          _ptr(dest_idx, "dest_idx", torch.int32, d.N),
                                          _ptr(dX, "dX", torch.float32, d.R * d.S * H), _stream(stream)))
+
+
+def moonep_swiglu(d: Dims, Hp: int, Ygu, A, stream=None):
+    t = _dtype_enum(Ygu)
+    _check(_LIB.moonep_swiglu(d, int(Hp), t, _ptr(Ygu, "Ygu", Ygu.dtype, d.N * 2 * Hp),
+                              _ptr(A, "A", Ygu.dtype, d.N * Hp), _stream(stream)))
+
+
+def moonep_swiglu_backward(d: Dims, Hp: int, Ygu, dA, dYgu, stream=None):
+    t = _dtype_enum(Ygu)
+    _check(_LIB.moonep_swiglu_backward(d, int(Hp), t, _ptr(Ygu, "Ygu", Ygu.dtype, d.N * 2 * Hp),
+                                       _ptr(dA, "dA", Ygu.dtype, d.N * Hp),
+                                       _ptr(dYgu, "dYgu", Ygu.dtype, d.N * 2 * Hp), _stream(stream)))

@@ -1,0 +1,191 @@
+// moonep_swiglu / moonep_swiglu_backward: the activation of the gated expert FFN.
+//
+// [P2] = "Moonshot open-sources MoonEP: an expert-parallel communication library
+// for MoE training" (umios.umi6.com), section "Memory contract and weight
+// layout": one [E+B, H, H'] tensor per expert projection.  The pages do not name
+// the FFN; read plainly it is the gated expert: a gate|up projection whose rows
+// hold [gate (H') | up (H')], act = silu(gate) * up, then a down projection.
+//
+// Both kernels are HBM streams over the N = R*S*K dispatched rows, one thread per
+// 16-byte chunk of the output row over a one-shot grid (one vector per thread
+// measured fastest for streams on this chip).  Arithmetic is float32 on the
+// (bf16 or f32) inputs; each result is rounded once to the row dtype.
+#include "moonep_common.h"
+
+namespace moonep {
+namespace {
+
+constexpr int kActThreads = 256;
+
+// sigmoid from exp of a non-positive argument only, so it never overflows
+__device__ __forceinline__ float sigmoid_f(float g) {
+  const float e = expf(-fabsf(g));
+  const float r = 1.f / (1.f + e);
+  return g >= 0.f ? r : e * r;
+}
+
+template <typename T>
+struct Vec;
+template <>
+struct Vec<uint16_t> {  // 8 bf16 per 16 bytes
+  static constexpr int N = 8;
+  static __device__ __forceinline__ void load(const uint16_t* p, float* f) {
+    const u32x4 q = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(q[i] << 16);
+      f[2 * i + 1] = __uint_as_float(q[i] & 0xffff0000u);
+    }
+  }
+  static __device__ __forceinline__ void store(uint16_t* p, const float* f) {
+    u32x4 q;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) q[i] = (uint32_t)f32_to_bf16(f[2 * i]) | ((uint32_t)f32_to_bf16(f[2 * i + 1]) << 16);
+    *reinterpret_cast<u32x4*>(p) = q;
+  }
+};
+template <>
+struct Vec<float> {  // 4 f32 per 16 bytes
+  static constexpr int N = 4;
+  static __device__ __forceinline__ void load(const float* p, float* f) {
+    const f32x4 q = *reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = q[i];
+  }
+  static __device__ __forceinline__ void store(float* p, const float* f) {
+    *reinterpret_cast<f32x4*>(p) = f32x4{f[0], f[1], f[2], f[3]};
+  }
+};
+
+template <typename T>
+__device__ __forceinline__ float ld1(const T* p);
+template <>
+__device__ __forceinline__ float ld1<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
+template <>
+__device__ __forceinline__ float ld1<float>(const float* p) { return *p; }
+template <typename T>
+__device__ __forceinline__ void st1(T* p, float v);
+template <>
+__device__ __forceinline__ void st1<uint16_t>(uint16_t* p, float v) { *p = f32_to_bf16(v); }
+template <>
+__device__ __forceinline__ void st1<float>(float* p, float v) { *p = v; }
+
+__device__ __forceinline__ float swiglu1(float g, float u) { return g * sigmoid_f(g) * u; }
+
+__device__ __forceinline__ void swiglu_grad1(float g, float u, float da, float& dg, float& du) {
+  const float s = sigmoid_f(g);
+  dg = da * u * s * (1.f + g * (1.f - s));
+  du = da * g * s;
+}
+
+// A[row, c] = silu(Ygu[row, c]) * Ygu[row, Hp + c]; one thread per 16-byte chunk of A.
+template <typename T>
+__global__ __launch_bounds__(kActThreads) void swiglu_vec(const T* __restrict__ Ygu, T* __restrict__ A,
+                                                          int64_t rows, int Hp) {
+  constexpr int V = Vec<T>::N;
+  const int cpr = Hp / V;
+  const int64_t i = (int64_t)blockIdx.x * kActThreads + threadIdx.x;
+  if (i >= rows * cpr) return;
+  const int64_t row = i / cpr;
+  const int c = (int)(i % cpr) * V;
+  float g[V], u[V], a[V];
+  Vec<T>::load(Ygu + row * 2 * Hp + c, g);
+  Vec<T>::load(Ygu + row * 2 * Hp + Hp + c, u);
+#pragma unroll
+  for (int j = 0; j < V; ++j) a[j] = swiglu1(g[j], u[j]);
+  Vec<T>::store(A + row * Hp + c, a);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kActThreads) void swiglu_bwd_vec(const T* __restrict__ Ygu, const T* __restrict__ dA,
+                                                              T* __restrict__ dYgu, int64_t rows, int Hp) {
+  constexpr int V = Vec<T>::N;
+  const int cpr = Hp / V;
+  const int64_t i = (int64_t)blockIdx.x * kActThreads + threadIdx.x;
+  if (i >= rows * cpr) return;
+  const int64_t row = i / cpr;
+  const int c = (int)(i % cpr) * V;
+  float g[V], u[V], d[V], dg[V], du[V];
+  Vec<T>::load(Ygu + row * 2 * Hp + c, g);
+  Vec<T>::load(Ygu + row * 2 * Hp + Hp + c, u);
+  Vec<T>::load(dA + row * Hp + c, d);
+#pragma unroll
+  for (int j = 0; j < V; ++j) swiglu_grad1(g[j], u[j], d[j], dg[j], du[j]);
+  Vec<T>::store(dYgu + row * 2 * Hp + c, dg);
+  Vec<T>::store(dYgu + row * 2 * Hp + Hp + c, du);
+}
+
+// Scalar fallbacks (rows that are not a whole number of 16-byte chunks).
+template <typename T>
+__global__ __launch_bounds__(kActThreads) void swiglu_scalar(const T* __restrict__ Ygu, T* __restrict__ A,
+                                                             int64_t rows, int Hp) {
+  const int64_t i = (int64_t)blockIdx.x * kActThreads + threadIdx.x;
+  if (i >= rows * Hp) return;
+  const int64_t row = i / Hp;
+  const int c = (int)(i % Hp);
+  st1(A + row * Hp + c, swiglu1(ld1(Ygu + row * 2 * Hp + c), ld1(Ygu + row * 2 * Hp + Hp + c)));
+}
+
+template <typename T>
+__global__ __launch_bounds__(kActThreads) void swiglu_bwd_scalar(const T* __restrict__ Ygu, const T* __restrict__ dA,
+                                                                 T* __restrict__ dYgu, int64_t rows, int Hp) {
+  const int64_t i = (int64_t)blockIdx.x * kActThreads + threadIdx.x;
+  if (i >= rows * Hp) return;
+  const int64_t row = i / Hp;
+  const int c = (int)(i % Hp);
+  float dg, du;
+  swiglu_grad1(ld1(Ygu + row * 2 * Hp + c), ld1(Ygu + row * 2 * Hp + Hp + c), ld1(dA + row * Hp + c), dg, du);
+  st1(dYgu + row * 2 * Hp + c, dg);
+  st1(dYgu + row * 2 * Hp + Hp + c, du);
+}
+
+template <typename T>
+int act_launch(const char* name, bool backward, int64_t rows, int Hp, const void* Ygu, const void* dA, void* out,
+               hipStream_t s) {
+  constexpr int V = Vec<T>::N;
+  const bool vec = Hp % V == 0 && aligned16(Ygu) && aligned16(out) && (!backward || aligned16(dA));
+  const int64_t items = vec ? rows * (Hp / V) : rows * Hp;
+  MOONEP_REQUIRE(items / kActThreads < (int64_t(1) << 31), "%s: grid too large", name);
+  const unsigned grid = ceil_div_u(items, kActThreads);
+  const T* y = static_cast<const T*>(Ygu);
+  T* o = static_cast<T*>(out);
+  if (!backward) {
+    if (vec) hipLaunchKernelGGL(swiglu_vec<T>, dim3(grid), dim3(kActThreads), 0, s, y, o, rows, Hp);
+    else hipLaunchKernelGGL(swiglu_scalar<T>, dim3(grid), dim3(kActThreads), 0, s, y, o, rows, Hp);
+  } else {
+    const T* d = static_cast<const T*>(dA);
+    if (vec) hipLaunchKernelGGL(swiglu_bwd_vec<T>, dim3(grid), dim3(kActThreads), 0, s, y, d, o, rows, Hp);
+    else hipLaunchKernelGGL(swiglu_bwd_scalar<T>, dim3(grid), dim3(kActThreads), 0, s, y, d, o, rows, Hp);
+  }
+  MOONEP_LAUNCH_CHECK(name);
+  return MOONEP_OK;
+}
+
+int act_entry(const char* name, bool backward, moonep_dims d, int32_t Hp, moonep_dtype t, const void* Ygu,
+              const void* dA, void* out, moonep_stream stream) {
+  if (int rc = check_dims(d, name)) return rc;
+  MOONEP_REQUIRE(t == MOONEP_F32 || t == MOONEP_BF16, "%s: bad dtype %d", name, (int)t);
+  MOONEP_REQUIRE(Hp >= 1, "%s: Hp must be >= 1", name);
+  const int64_t rows = n_pairs(d);
+  if (rows == 0) return MOONEP_OK;
+  MOONEP_REQUIRE(Ygu && out && (!backward || dA), "%s: null pointer", name);
+  hipStream_t s = as_stream(stream);
+  clear_stale_error();
+  return t == MOONEP_BF16 ? act_launch<uint16_t>(name, backward, rows, Hp, Ygu, dA, out, s)
+                          : act_launch<float>(name, backward, rows, Hp, Ygu, dA, out, s);
+}
+
+}  // namespace
+}  // namespace moonep
+
+using namespace moonep;
+
+extern "C" int moonep_swiglu(moonep_dims d, int32_t Hp, moonep_dtype t, const void* Ygu, void* A,
+                             moonep_stream stream) {
+  return act_entry("moonep_swiglu", false, d, Hp, t, Ygu, nullptr, A, stream);
+}
+
+extern "C" int moonep_swiglu_backward(moonep_dims d, int32_t Hp, moonep_dtype t, const void* Ygu, const void* dA,
+                                      void* dYgu, moonep_stream stream) {
+  return act_entry("moonep_swiglu_backward", true, d, Hp, t, Ygu, dA, dYgu, stream);
+}

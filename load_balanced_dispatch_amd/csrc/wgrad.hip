@@ -187,7 +187,7 @@ __global__ __launch_bounds__(512, 1) void wgrad_bf16(const uint16_t* __restrict_
   __shared__ int32_t s_unit[2];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int wm = w >> 2, wn = w & 3;
-  const int HT = H / BH, NT = (Hp + BN - 1) / BN;
+  const int HT = (H + BH - 1) / BH, NT = (Hp + BN - 1) / BN;  // H % 128 == 0, H' % 64 == 0
   const int per_job = HT * NT;
   const int J = E + R * B;
   const int n = ws[0];
@@ -221,7 +221,9 @@ __global__ __launch_bounds__(512, 1) void wgrad_bf16(const uint16_t* __restrict_
     const int nchunks = sorted_chunks[pos];
     const int h0 = (tile / NT) * BH, n0 = (tile % NT) * BN;
     const int width = min(BN, Hp - n0);
-    const bool wave_cols = wn * WN < width;
+    // a partial tile (H % 256 or H' % 256 != 0) leaves whole 128-row or 64-column wave strips idle;
+    // they still issue their share of the DMA and take every barrier
+    const bool wave_cols = wn * WN < width && wm * 128 < min(BH, H - h0);
     float* out = job < E ? dW_home + (int64_t)job * H * Hp : dW_slots + (int64_t)(job - E) * H * Hp;
 
     // DMA slices: instruction j = 2w+i fills rows 2j, 2j+1 of the X stage, then of the D stage
@@ -243,7 +245,7 @@ __global__ __launch_bounds__(512, 1) void wgrad_bf16(const uint16_t* __restrict_
       for (int i = 0; i < 2; ++i) {
         const int row = walk.m + src_row[i];
         const bool ok = row < walk.end;
-        const uint16_t* xs = ok ? Xp + (int64_t)row * H + h0 + x_col[i] : zero_row + x_col[i];
+        const uint16_t* xs = ok ? Xp + (int64_t)row * H + min(h0 + x_col[i], H - 8) : zero_row + x_col[i];
         const int dc = min(n0 + d_col[i], Hp - 8);
         const uint16_t* ds = ok ? dY + (int64_t)row * Hp + dc : zero_row + d_col[i];
         dma16(xs, st + (2 * w + i) * 512);
@@ -450,11 +452,11 @@ extern "C" int moonep_wgrad(moonep_dims d, int32_t H, int32_t Hp, moonep_dtype t
   const int64_t jobs = (int64_t)d.E + (int64_t)d.R * d.B;
   MOONEP_REQUIRE(jobs < (int64_t(1) << 28), "moonep_wgrad: too many jobs");
   const int P = d.S * d.K;
-  const bool mfma = t == MOONEP_BF16 && H % wg::BH == 0 && Hp % 64 == 0 && aligned16(Xp) && aligned16(dY) &&
+  const bool mfma = t == MOONEP_BF16 && H % 128 == 0 && Hp % 64 == 0 && aligned16(Xp) && aligned16(dY) &&
                     aligned16(dW_home) && (d.B == 0 || aligned16(dW_slots));
   if (mfma) {
     const int cus = device_cu_count();
-    const int64_t units = jobs * (H / wg::BH) * ((Hp + wg::BN - 1) / wg::BN);
+    const int64_t units = jobs * ((H + wg::BH - 1) / wg::BH) * ((Hp + wg::BN - 1) / wg::BN);
     MOONEP_REQUIRE(units + 8 * (int64_t)cus < (int64_t(1) << 30), "moonep_wgrad: too many output tiles");
     int32_t* ws = static_cast<int32_t*>(workspace);
     hipLaunchKernelGGL(wgrad_schedule, dim3(1), dim3(1024), 0, s, cu_seqlens, d.R, d.E, d.B, ws);

@@ -115,3 +115,113 @@ class MoeLayer:
     def backward(self, stream=None):
         self.wgrad(stream)
         self.reduce_grad(stream)
+
+
+class MoeFFN:
+    """Static buffers for one balanced MoE layer whose experts are gated FFNs, and the call sequence.
+
+    Forward: plan -> dispatch -> prefetch (both projections) -> group GEMM with the gate|up weights
+    [E+B, H, 2H'] -> swiglu -> group GEMM with the down weights [E+B, H', H] -> combine to [R, S, H].
+    Backward (backward=True): combine backward -> dgrad and wgrad of the down projection -> swiglu
+    backward -> dgrad and wgrad of the gate|up projection -> dispatch backward -> reduce_grad of both
+    projections.  Every buffer has a shape fixed by (R, E, B, S, K, H, H'); nothing depends on the
+    routing, so passes allocate nothing.
+    """
+
+    def __init__(self, R, E, B, S, K, H, Hp, dtype=torch.bfloat16, device="cuda", backward=False):
+        self.d: Dims = make_dims(R, E, B, S, K)
+        d = self.d
+        self.H, self.Hp, self.dtype, self.device = H, Hp, dtype, device
+        i32 = dict(dtype=torch.int32, device=device)
+        act = dict(dtype=dtype, device=device)
+        f32 = dict(dtype=torch.float32, device=device)
+        N = d.N
+        self.topk_idx = torch.zeros((R, S, K), **i32)
+        self.gates = torch.zeros((R, S, K), **f32)
+        self.expert_counts = torch.zeros(E, **i32)
+        self.maxvio = torch.zeros(1, dtype=torch.float64, device=device)
+        self.cu_seqlens = torch.zeros((R, E + B + 1), **i32)
+        self.slot_expert = torch.full((R, max(B, 0)), -1, **i32)
+        self.dest_idx = torch.zeros((R, S, K), **i32)
+        self.stats = torch.zeros(4, **i32)
+        self.ws_plan = torch.empty(max(1, _lib.moonep_plan_workspace_bytes(d)), dtype=torch.uint8, device=device)
+        self.ws_gemm = torch.empty(max(1, _lib.moonep_group_gemm_workspace_bytes(d)), dtype=torch.uint8,
+                                   device=device)
+        self.X = torch.zeros((R, S, H), **act)
+        self.Xp = torch.empty((N, H), **act)
+        self.W_gu_home = torch.zeros((E, H, 2 * Hp), **act)
+        self.W_gu_slots = torch.zeros((R, B, H, 2 * Hp), **act)
+        self.W_down_home = torch.zeros((E, Hp, H), **act)
+        self.W_down_slots = torch.zeros((R, B, Hp, H), **act)
+        self.Ygu = torch.empty((N, 2 * Hp), **act)
+        self.A = torch.empty((N, Hp), **act)
+        self.Zp = torch.empty((N, H), **act)
+        self.out = torch.empty((R, S, H), **f32)
+        if backward:
+            self.ws_wgrad = torch.empty(max(1, _lib.moonep_wgrad_workspace_bytes(d)), dtype=torch.uint8,
+                                        device=device)
+            self.dout = torch.zeros((R, S, H), **f32)
+            self.dgates = torch.zeros((R, S, K), **f32)
+            self.dZp = torch.empty((N, H), **act)
+            self.dA = torch.empty((N, Hp), **act)
+            self.dYgu = torch.empty((N, 2 * Hp), **act)
+            self.dXp = torch.empty((N, H), **act)
+            self.dX = torch.empty((R, S, H), **f32)
+            self.dW_gu_home = torch.zeros((E, H, 2 * Hp), **f32)
+            self.dW_gu_slots = torch.zeros((R, B, H, 2 * Hp), **f32)
+            self.dW_down_home = torch.zeros((E, Hp, H), **f32)
+            self.dW_down_slots = torch.zeros((R, B, Hp, H), **f32)
+
+    def _slots(self, t):
+        return t if self.d.B > 0 else None
+
+    def forward_calls(self):
+        d, H, Hp, L = self.d, self.H, self.Hp, _lib
+        sl = self._slots
+        return [
+            ("plan", lambda: L.moonep_plan(d, self.topk_idx, self.expert_counts, self.maxvio, self.cu_seqlens,
+                                           sl(self.slot_expert), self.dest_idx, None, self.stats, self.ws_plan)),
+            ("dispatch", lambda: L.moonep_dispatch(d, H, self.X, self.dest_idx, self.Xp)),
+            ("prefetch", lambda: (L.moonep_prefetch(d, H, 2 * Hp, self.W_gu_home, sl(self.slot_expert),
+                                                    sl(self.W_gu_slots)),
+                                  L.moonep_prefetch(d, Hp, H, self.W_down_home, sl(self.slot_expert),
+                                                    sl(self.W_down_slots)))),
+            ("gemm_gate_up", lambda: L.moonep_group_gemm(d, H, 2 * Hp, self.Xp, self.W_gu_home, sl(self.W_gu_slots),
+                                                         self.cu_seqlens, self.Ygu, self.ws_gemm)),
+            ("swiglu", lambda: L.moonep_swiglu(d, Hp, self.Ygu, self.A)),
+            ("gemm_down", lambda: L.moonep_group_gemm(d, Hp, H, self.A, self.W_down_home, sl(self.W_down_slots),
+                                                      self.cu_seqlens, self.Zp, self.ws_gemm)),
+            ("combine", lambda: L.moonep_combine(d, H, self.Zp, self.dest_idx, self.gates, self.out)),
+        ]
+
+    def backward_calls(self):
+        d, H, Hp, L = self.d, self.H, self.Hp, _lib
+        sl = self._slots
+        return [
+            ("combine_backward", lambda: L.moonep_combine_backward(d, H, self.dout, self.Zp, self.dest_idx,
+                                                                   self.gates, self.dZp, self.dgates)),
+            ("dgrad_down", lambda: L.moonep_group_gemm_dgrad(d, Hp, H, self.dZp, self.W_down_home,
+                                                             sl(self.W_down_slots), self.cu_seqlens, self.dA,
+                                                             self.ws_gemm)),
+            ("wgrad_down", lambda: L.moonep_wgrad(d, Hp, H, self.A, self.dZp, self.cu_seqlens, self.dW_down_home,
+                                                  sl(self.dW_down_slots), self.ws_wgrad)),
+            ("swiglu_backward", lambda: L.moonep_swiglu_backward(d, Hp, self.Ygu, self.dA, self.dYgu)),
+            ("dgrad_gate_up", lambda: L.moonep_group_gemm_dgrad(d, H, 2 * Hp, self.dYgu, self.W_gu_home,
+                                                                sl(self.W_gu_slots), self.cu_seqlens, self.dXp,
+                                                                self.ws_gemm)),
+            ("wgrad_gate_up", lambda: L.moonep_wgrad(d, H, 2 * Hp, self.Xp, self.dYgu, self.cu_seqlens,
+                                                     self.dW_gu_home, sl(self.dW_gu_slots), self.ws_wgrad)),
+            ("dispatch_backward", lambda: L.moonep_dispatch_backward(d, H, self.dXp, self.dest_idx, self.dX)),
+            ("reduce_grad", lambda: (L.moonep_reduce_grad(d, H, 2 * Hp, sl(self.slot_expert), self.dW_gu_home,
+                                                          sl(self.dW_gu_slots)),
+                                     L.moonep_reduce_grad(d, Hp, H, sl(self.slot_expert), self.dW_down_home,
+                                                          sl(self.dW_down_slots)))),
+        ]
+
+    def forward(self):
+        for _, f in self.forward_calls():
+            f()
+
+    def backward(self):
+        for _, f in self.backward_calls():
+            f()

@@ -26,6 +26,7 @@ import numpy as np
 
 # Stream tags: every tensor draws from its own seeded stream.
 TAG_SKEW, TAG_LOGITS, TAG_PERM, TAG_X, TAG_W, TAG_DY, TAG_MISC = 1, 2, 3, 4, 5, 6, 7
+TAG_WD = 8  # second projection's weights (the down projection of the gated FFN)
 
 
 def _rng(seed: int, tag: int, sub: int = 0) -> np.random.Generator:

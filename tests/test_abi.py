@@ -21,7 +21,7 @@ def test_header_declares_the_calls():
     syms = declared_symbols()
     for name in ("moonep_plan", "moonep_dispatch", "moonep_prefetch", "moonep_group_gemm", "moonep_combine",
                  "moonep_wgrad", "moonep_reduce_grad", "moonep_combine_backward", "moonep_group_gemm_dgrad",
-                 "moonep_dispatch_backward"):
+                 "moonep_dispatch_backward", "moonep_swiglu", "moonep_swiglu_backward"):
         assert name in syms
 
 
@@ -63,6 +63,8 @@ def test_bad_dims_rejected_everywhere(dims, msg):
         lambda: L.moonep_combine_backward(d, 8, 1, *([null] * 7)),
         lambda: L.moonep_group_gemm_dgrad(d, 8, 8, 1, *([null] * 7)),
         lambda: L.moonep_dispatch_backward(d, 8, 1, null, null, null, null),
+        lambda: L.moonep_swiglu(d, 8, 1, null, null, null),
+        lambda: L.moonep_swiglu_backward(d, 8, 1, null, null, null, null),
     ]
     for c in calls:
         assert c() == _lib.MOONEP_EINVAL
@@ -83,6 +85,8 @@ def test_null_pointers_rejected():
     assert L.moonep_combine_backward(d, 8, 1, *([None] * 7)) == _lib.MOONEP_EINVAL
     assert L.moonep_group_gemm_dgrad(d, 8, 8, 1, *([None] * 7)) == _lib.MOONEP_EINVAL
     assert L.moonep_dispatch_backward(d, 8, 1, None, None, None, None) == _lib.MOONEP_EINVAL
+    assert L.moonep_swiglu(d, 8, 1, None, None, None) == _lib.MOONEP_EINVAL
+    assert L.moonep_swiglu_backward(d, 8, 1, None, None, None, None) == _lib.MOONEP_EINVAL
 
 
 def test_bad_dtype_rejected():
@@ -107,6 +111,8 @@ def test_empty_work_is_a_no_op():
     assert L.moonep_combine_backward(d, 8, 1, *([None] * 7)) == _lib.MOONEP_OK
     assert L.moonep_group_gemm_dgrad(d, 8, 8, 1, *([None] * 7)) == _lib.MOONEP_OK
     assert L.moonep_dispatch_backward(d, 8, 1, None, None, None, None) == _lib.MOONEP_OK
+    assert L.moonep_swiglu(d, 8, 1, None, None, None) == _lib.MOONEP_OK
+    assert L.moonep_swiglu_backward(d, 8, 1, None, None, None, None) == _lib.MOONEP_OK
 
 
 def test_binding_refuses_host_tensors():
