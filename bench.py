@@ -159,6 +159,59 @@ def time_next_rows(L, steps, warmup):
             for i, (n, _) in enumerate(calls)}
 
 
+def time_ffn(wl, seed, alpha, steps, warmup):
+    """The full gated expert FFN (NEXT row) on the workload's dims: gate|up [E+B, H, 2H'], swiglu,
+    down [E+B, H', H], forward then backward, every call bracketed by HIP events."""
+    import torch
+
+    import load_balanced_dispatch_amd as m
+    from synthetic.router import TAG_W, TAG_WD, TAG_X, normal_tensor, router_output
+    R, E, B, S, K, H, Hp = wl.R, wl.E, wl.B, wl.S, wl.K, wl.H, wl.Hp
+    F = m.MoeFFN(R, E, B, S, K, H, Hp, backward=True)
+    idx, gates = router_output(R, S, E, K, seed, alpha=alpha, zipf_s=wl.zipf_s)
+    F.topk_idx.copy_(torch.as_tensor(idx))
+    F.gates.copy_(torch.as_tensor(gates))
+    F.X.copy_(normal_tensor((R, S, H), 1.0, "bf16", seed, TAG_X, "cuda", slices=R))
+    F.W_gu_home.copy_(normal_tensor((E, H, 2 * Hp), H ** -0.5, "bf16", seed, TAG_W, "cuda", slices=E))
+    F.W_down_home.copy_(normal_tensor((E, Hp, H), Hp ** -0.5, "bf16", seed, TAG_WD, "cuda", slices=E))
+    F.dout.normal_(generator=torch.Generator(device="cuda").manual_seed(seed + 11))
+    calls = F.forward_calls() + F.backward_calls()
+    for _ in range(warmup):
+        for _, f in calls:
+            f()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(steps)]
+    for st in range(steps):
+        evs[st][0].record()
+        for i, (_, f) in enumerate(calls):
+            f()
+            evs[st][i + 1].record()
+    torch.cuda.synchronize()
+    ms = {n: sum(evs[st][i].elapsed_time(evs[st][i + 1]) for st in range(steps)) / steps
+          for i, (n, _) in enumerate(calls)}
+    nf = len(F.forward_calls())
+    fwd = sum(v for i, v in enumerate(ms.values()) if i < nf)
+    bwd = sum(v for i, v in enumerate(ms.values()) if i >= nf)
+    N, b = wl.N, 2
+    gemm_flops = {"gemm_gate_up": 2 * N * H * 2 * Hp, "gemm_down": 2 * N * Hp * H, "dgrad_down": 2 * N * Hp * H,
+                  "wgrad_down": 2 * N * Hp * H, "dgrad_gate_up": 2 * N * H * 2 * Hp, "wgrad_gate_up": 2 * N * H * 2 * Hp}
+    act_bytes = {"swiglu": 3 * N * Hp * b, "swiglu_backward": 5 * N * Hp * b}
+    out = {"forward_ms": round(fwd, 4), "backward_ms": round(bwd, 4),
+           "gemm_tflops": round(sum(gemm_flops.values()) / (sum(ms[k] for k in gemm_flops) * 1e-3) / 1e12, 2),
+           "stages_ms": {k: round(v, 4) for k, v in ms.items()}}
+    for k, fl in gemm_flops.items():
+        a = fl / (ms[k] * 1e-3) / 1e12
+        out[k] = {"bound": "mfma", "achieved": round(a, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                  "frac": round(a / MFMA_BF16_PEAK_TFLOPS, 4), "avg_launch_ms": round(ms[k], 4)}
+    for k, by in act_bytes.items():
+        a = by / (ms[k] * 1e-3) / 1e9
+        out[k] = {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                  "frac": round(a / HBM_PEAK_GBS, 4), "avg_launch_ms": round(ms[k], 4)}
+    del F
+    torch.cuda.empty_cache()
+    return out
+
+
 def algorithmic(wl, stats, slot_expert_np, L):
     """Algorithmic work per launch of each stage: bytes for the bandwidth-bound stages (every input byte
     read once, every output byte written once), flops for the two GEMMs plus the least HBM bytes they can
@@ -202,10 +255,13 @@ STAGE_KERNELS = {
     "combine_backward": r"^combine_bwd_",
     "dgrad": r"^(ggemm_bf16<true>|ggemm_generic<.*true>)",
     "dispatch_backward": r"^combine_(vec|scalar)<.*false>",
+    "swiglu": r"^swiglu_(vec|scalar)<",
+    "swiglu_backward": r"^swiglu_bwd_",
 }
 STAGE_SOURCE = {"plan": "plan.hip", "dispatch": "move.hip", "prefetch": "move.hip", "group_gemm": "ggemm.hip",
                 "combine": "move.hip", "wgrad": "wgrad.hip", "reduce_grad": "move.hip",
-                "combine_backward": "move.hip", "dgrad": "ggemm.hip", "dispatch_backward": "move.hip"}
+                "combine_backward": "move.hip", "dgrad": "ggemm.hip", "dispatch_backward": "move.hip",
+                "swiglu": "act.hip", "swiglu_backward": "act.hip"}
 GEMM_STAGES = ("group_gemm", "wgrad", "dgrad")
 NEXT_STAGES = ("combine_backward", "dgrad", "dispatch_backward")
 CSRC = os.path.join(ROOT, "load_balanced_dispatch_amd", "csrc")
@@ -484,6 +540,11 @@ def main():
         nx = time_next_rows(L, args.steps, args.warmup)
         log(f"backward of the data path: {nx}")
         next_rows = {n: stage_roofline(n, alg, nx[n], traffic, wl.dtype == "f32") for n in nx}
+        if wl.dtype == "bf16":
+            log("full gated expert FFN (forward + backward)")
+            next_rows["ffn"] = time_ffn(wl, args.seed, h["alpha"], max(3, args.steps // 4), 2)
+            next_rows["ffn"]["workload"] = (f"gate|up [E+B, {wl.H}, {2 * wl.Hp}], swiglu, down [E+B, {wl.Hp}, "
+                                            f"{wl.H}] on the same routing")
     dominant = max(st, key=lambda n: st[n])
     roofline = dict(rooflines[dominant], stage=dominant)
 
