@@ -51,6 +51,7 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--forward-only", action="store_true")
+    ap.add_argument("--no-ffn", action="store_true", help="skip the full gated expert FFN in next_rows")
     ap.add_argument("--stats-md", metavar="CSV",
                     help="print a markdown table of the library kernels in a rocprofv3 kernel_stats.csv; no GPU")
     ap.add_argument("--traffic-md", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -540,7 +541,7 @@ def main():
         nx = time_next_rows(L, args.steps, args.warmup)
         log(f"backward of the data path: {nx}")
         next_rows = {n: stage_roofline(n, alg, nx[n], traffic, wl.dtype == "f32") for n in nx}
-        if wl.dtype == "bf16":
+        if wl.dtype == "bf16" and not args.no_ffn:
             log("full gated expert FFN (forward + backward)")
             next_rows["ffn"] = time_ffn(wl, args.seed, h["alpha"], max(3, args.steps // 4), 2)
             next_rows["ffn"]["workload"] = (f"gate|up [E+B, {wl.H}, {2 * wl.Hp}], swiglu, down [E+B, {wl.Hp}, "

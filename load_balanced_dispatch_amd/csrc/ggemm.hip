@@ -97,6 +97,7 @@ __device__ __forceinline__ int find_group(const int32_t* tstart, int NG, int mt)
 namespace fwd {
 constexpr int BM = 256, BN = 256, BK = 32, STAGES = 4, NWAVES = 8;
 constexpr int OPS = 4;  // DMA instructions per wave per stage (2 for A, 2 for B)
+constexpr int kBandM = 4;  // m-tiles per band of the tile raster
 constexpr int A_STAGE = BM * BK;  // 64-byte rows; 16-byte chunks XOR-swizzled by row
 constexpr int B_STAGE = BK * BN;  // 512-byte rows; 64-byte blocks XOR-swizzled by row
 constexpr int STAGE = A_STAGE + B_STAGE;
@@ -121,9 +122,10 @@ __device__ __forceinline__ int b_off(int k, int n) { return k * BN + ((((n >> 5)
 // W row), so it is staged and read exactly like the activation tile; otherwise it is k-major and
 // read with the transpose read.
 //
-// Persistent: one 512-thread block per CU; tile ids are remapped so the blocks of one XCD
-// (workgroups are dealt to the 8 XCDs round-robin) take consecutive tiles, which share token rows
-// and expert weights in that XCD's L2.  Block tile 256 x 256 x 32; eight waves of 128 x 64
+// Persistent: one 512-thread block per CU; block ids are remapped so the blocks of one XCD
+// (workgroups are dealt to the 8 XCDs round-robin) take consecutive tile ids, and tile ids follow
+// a banded raster (4 m-tiles x all n-tiles per band, n-major inside), so those tiles share token
+// rows and expert weights in that XCD's L2.  Block tile 256 x 256 x 32; eight waves of 128 x 64
 // (MFMA 32x32x16 bf16, two waves per SIMD).  Operand tiles stream global -> LDS with
 // global_load_lds_dwordx4 into a 4-stage ring, three stages ahead of the MFMAs, with no
 // register staging.  The last n-tile may be narrower than 256 (H' % 256 != 0): its missing
@@ -148,8 +150,13 @@ __global__ __launch_bounds__(512, 1) void ggemm_bf16(const uint16_t* __restrict_
   const int a_lr = lane >> 2, a_ls = lane & 3;   // A: one wave instruction fills 16 rows
   const int b_lr = lane >> 5, b_ls = lane & 31;  // B: one wave instruction fills 2 rows
 
+  const int MT = tstart[NG];
   for (int tile = vb; tile < total; tile += nblk) {
-    const int mt = tile / NT, nt = tile % NT;
+    // banded raster: bands of kBandM consecutive m-tiles, n-tile-major inside a band, so the 32
+    // tiles one XCD runs at once cover a kBandM x 8 block and reuse both operands in its L2
+    const int band = tile / (kBandM * NT), m0b = band * kBandM;
+    const int sb = min(kBandM, MT - m0b), rb = tile - band * kBandM * NT;
+    const int mt = m0b + rb % sb, nt = rb / sb;
     const int grp = find_group(tstart, NG, mt);
     const int r = grp / G, g = grp % G;
     const int c0 = cu[(int64_t)r * G1 + g], c1 = cu[(int64_t)r * G1 + g + 1];
