@@ -139,6 +139,8 @@ __global__ __launch_bounds__(512, 1) void ggemm_bf16(const uint16_t* __restrict_
                                                      int R, int E, int B, int P, int H, int Hp) {
   __shared__ __attribute__((aligned(1024))) uint16_t lds[LDS_ELEMS];
   const int K = BT ? Hp : H, N = BT ? H : Hp;  // reduction length and output width
+  const uint32_t lds0 = lds_addr(lds);                            // LDS byte address of the ring
+  const int wu = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, uniform
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int wm = w >> 2, wn = w & 3;
   const int G = E + B, G1 = G + 1, NG = R * G;
@@ -189,12 +191,12 @@ __global__ __launch_bounds__(512, 1) void ggemm_bf16(const uint16_t* __restrict_
       }
     }
     const int64_t b_step = BT ? BK : (int64_t)BK * Hp;  // one stage along k
-    auto issue = [&](int kt) {
-      uint16_t* st = lds + (kt % STAGES) * STAGE;
+    auto issue = [&](int kt) {  // this wave's 1 KB pieces of stage kt: slot byte base + (2w + i) KB
+      const uint32_t st = lds0 + (uint32_t)((kt % STAGES) * STAGE * 2 + wu * 2 * 1024);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) dma16(a_src[i] + kt * BK, st + (2 * w + i) * 512);
+      for (int i = 0; i < 2; ++i) dma16(a_src[i] + kt * BK, st + i * 1024);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) dma16(b_src[i] + kt * b_step, st + A_STAGE + (2 * w + i) * 512);
+      for (int i = 0; i < 2; ++i) dma16(b_src[i] + kt * b_step, st + A_STAGE * 2 + i * 1024);
     };
 
     f32x16 acc[TM][TN];

@@ -45,14 +45,21 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// 64 lanes x 16 bytes: lane l copies 16 bytes from its global address g to LDS at
-// lds_wave_base + 16*l (global_load_lds_dwordx4; lds_wave_base must be wave-uniform).  Issued
-// from asm so the compiler does not wait for every outstanding load before each LDS read: the
-// kernels wait on vmcnt themselves (wait_vmcnt) before a barrier.
+// 64 lanes x 16 bytes: lane l copies 16 bytes from its global address g to LDS byte address
+// lds_byte + 16*l (global_load_lds_dwordx4; lds_byte must be wave-uniform).  Issued from asm so
+// the compiler does not wait for every outstanding load before each LDS read: the kernels wait on
+// vmcnt themselves (wait_vmcnt) before a barrier.  The destination is an LDS byte address the
+// caller computes as base + offset (lds_addr once per kernel), not a pointer: converting a pointer
+// back to the LDS address space costs a null check per instruction, which measured 4-8% on the
+// GEMMs' memory phases.
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
-__device__ __forceinline__ void dma16(const void* g, uint16_t* lds_wave_base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_u16*)lds_wave_base);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_byte) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_byte) : "memory", "m0");
+}
+
+// LDS byte address of (an element of) a shared array, wave-uniform.
+__device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_u16*)p);
 }
 
 // Waits until at most N of this wave's vector-memory operations are outstanding (they retire in order).

@@ -194,6 +194,8 @@ __global__ __launch_bounds__(512, 1) void wgrad_bf16(const uint16_t* __restrict_
   const int32_t* sorted_job = ws + kSchedHdr;
   const int32_t* sorted_chunks = sorted_job + J;
   const int home_q = blockIdx.x % kQueues;
+  const uint32_t lds0 = lds_addr(lds);                            // LDS byte address of the ring
+  const int wu = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, uniform
   int qd = 0;  // thread 0: queues home_q .. home_q + qd - 1 (mod 8) are known to be empty
 
   for (;;) {
@@ -240,7 +242,7 @@ __global__ __launch_bounds__(512, 1) void wgrad_bf16(const uint16_t* __restrict_
     walk.seek(walk.r);
     int issued = 0;
     auto issue_next = [&]() {  // DMA of chunk `issued` into its ring slot, then advance the walker
-      uint16_t* st = lds + (issued % STAGES) * STAGE;
+      const uint32_t st = lds0 + (uint32_t)((issued % STAGES) * STAGE * 2 + wu * 2 * 1024);  // + (2w + i) KB
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int row = walk.m + src_row[i];
@@ -248,8 +250,8 @@ __global__ __launch_bounds__(512, 1) void wgrad_bf16(const uint16_t* __restrict_
         const uint16_t* xs = ok ? Xp + (int64_t)row * H + min(h0 + x_col[i], H - 8) : zero_row + x_col[i];
         const int dc = min(n0 + d_col[i], Hp - 8);
         const uint16_t* ds = ok ? dY + (int64_t)row * Hp + dc : zero_row + d_col[i];
-        dma16(xs, st + (2 * w + i) * 512);
-        dma16(ds, st + X_STAGE + (2 * w + i) * 512);
+        dma16(xs, st + i * 1024);
+        dma16(ds, st + X_STAGE * 2 + i * 1024);
       }
       ++issued;
       walk.next(BK);
