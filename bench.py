@@ -57,6 +57,13 @@ def parse():
     ap.add_argument("--traffic-md", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print the per-stage HBM traffic summary of two --profile-pass counter runs "
                          "(FETCH_SIZE, WRITE_SIZE) for --workload/--maxvio; no GPU")
+    ap.add_argument("--ffn-only", action="store_true",
+                    help="time only the full gated expert FFN and print its object (not the bench line); with "
+                         "--profile-pass, run its passes for counter runs instead")
+    ap.add_argument("--ffn-stats-md", metavar="TRACE_CSV",
+                    help="print per-call kernel times of an --ffn-only rocprofv3 kernel_trace.csv; no GPU")
+    ap.add_argument("--ffn-traffic-md", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="print the per-call HBM traffic of two --ffn-only --profile-pass counter runs; no GPU")
     ap.add_argument("--profile-pass", action="store_true",
                     help="for counter runs: 1 warm-up + --steps steps of the whole path, then one plain 1 GiB "
                          "device copy whose FETCH_SIZE/WRITE_SIZE calibrate the traffic counters; prints no JSON")
@@ -160,9 +167,22 @@ def time_next_rows(L, steps, warmup):
             for i, (n, _) in enumerate(calls)}
 
 
-def time_ffn(wl, seed, alpha, steps, warmup):
-    """The full gated expert FFN (NEXT row) on the workload's dims: gate|up [E+B, H, 2H'], swiglu,
-    down [E+B, H', H], forward then backward, every call bracketed by HIP events."""
+# Library kernel dispatches of each call of one full-FFN pass, in call order, and the stages those
+# kernels belong to; labels each dispatch of an FFN-only profile with the call that launched it.
+FFN_CALLS = [("plan", 4, ("plan",)), ("dispatch", 1, ("dispatch",)), ("prefetch", 2, ("prefetch",)),
+             ("gemm_gate_up", 2, ("group_gemm",)), ("swiglu", 1, ("swiglu",)), ("gemm_down", 2, ("group_gemm",)),
+             ("combine", 1, ("combine",)), ("combine_backward", 1, ("combine_backward",)),
+             ("dgrad_down", 2, ("group_gemm", "dgrad")), ("wgrad_down", 2, ("wgrad",)),
+             ("swiglu_backward", 1, ("swiglu_backward",)), ("dgrad_gate_up", 2, ("group_gemm", "dgrad")),
+             ("wgrad_gate_up", 2, ("wgrad",)), ("dispatch_backward", 1, ("dispatch_backward",)),
+             ("reduce_grad", 2, ("reduce_grad",))]
+FFN_GEMM_FLOPS = {"gemm_gate_up": 4, "gemm_down": 2, "dgrad_down": 2, "wgrad_down": 2, "dgrad_gate_up": 4,
+                  "wgrad_gate_up": 4}  # x N*H*H'
+FFN_ACT_BYTES = {"swiglu": 3, "swiglu_backward": 5}  # x N*H'*b
+
+
+def make_ffn(wl, seed, alpha):
+    """A MoeFFN on the workload's dims with its inputs drawn, and its forward + backward call list."""
     import torch
 
     import load_balanced_dispatch_amd as m
@@ -177,6 +197,17 @@ def time_ffn(wl, seed, alpha, steps, warmup):
     F.W_down_home.copy_(normal_tensor((E, Hp, H), Hp ** -0.5, "bf16", seed, TAG_WD, "cuda", slices=E))
     F.dout.normal_(generator=torch.Generator(device="cuda").manual_seed(seed + 11))
     calls = F.forward_calls() + F.backward_calls()
+    assert [n for n, _ in calls] == [c[0] for c in FFN_CALLS]
+    return F, calls
+
+
+def time_ffn(wl, seed, alpha, steps, warmup):
+    """The full gated expert FFN (NEXT row) on the workload's dims: gate|up [E+B, H, 2H'], swiglu,
+    down [E+B, H', H], forward then backward, every call bracketed by HIP events."""
+    import torch
+
+    R, E, B, S, K, H, Hp = wl.R, wl.E, wl.B, wl.S, wl.K, wl.H, wl.Hp
+    F, calls = make_ffn(wl, seed, alpha)
     for _ in range(warmup):
         for _, f in calls:
             f()
@@ -194,20 +225,21 @@ def time_ffn(wl, seed, alpha, steps, warmup):
     fwd = sum(v for i, v in enumerate(ms.values()) if i < nf)
     bwd = sum(v for i, v in enumerate(ms.values()) if i >= nf)
     N, b = wl.N, 2
-    gemm_flops = {"gemm_gate_up": 2 * N * H * 2 * Hp, "gemm_down": 2 * N * Hp * H, "dgrad_down": 2 * N * Hp * H,
-                  "wgrad_down": 2 * N * Hp * H, "dgrad_gate_up": 2 * N * H * 2 * Hp, "wgrad_gate_up": 2 * N * H * 2 * Hp}
-    act_bytes = {"swiglu": 3 * N * Hp * b, "swiglu_backward": 5 * N * Hp * b}
+    gemm_flops = {k: c * N * H * Hp for k, c in FFN_GEMM_FLOPS.items()}
+    act_bytes = {k: c * N * Hp * b for k, c in FFN_ACT_BYTES.items()}
+    traffic = load_ffn_traffic(wl)
     out = {"forward_ms": round(fwd, 4), "backward_ms": round(bwd, 4),
            "gemm_tflops": round(sum(gemm_flops.values()) / (sum(ms[k] for k in gemm_flops) * 1e-3) / 1e12, 2),
            "stages_ms": {k: round(v, 4) for k, v in ms.items()}}
     for k, fl in gemm_flops.items():
         a = fl / (ms[k] * 1e-3) / 1e12
         out[k] = {"bound": "mfma", "achieved": round(a, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                  "frac": round(a / MFMA_BF16_PEAK_TFLOPS, 4), "avg_launch_ms": round(ms[k], 4)}
+                  "frac": round(a / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic.get(k),
+                  "avg_launch_ms": round(ms[k], 4)}
     for k, by in act_bytes.items():
         a = by / (ms[k] * 1e-3) / 1e9
         out[k] = {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                  "frac": round(a / HBM_PEAK_GBS, 4), "avg_launch_ms": round(ms[k], 4)}
+                  "frac": round(a / HBM_PEAK_GBS, 4), "traffic": traffic.get(k), "avg_launch_ms": round(ms[k], 4)}
     del F
     torch.cuda.empty_cache()
     return out
@@ -300,7 +332,12 @@ def stage_of(base):
 
 def sources_digest(stage):
     """Hash of the source a stage's kernels are compiled from (its .hip file and every csrc header)."""
-    files = [os.path.join(CSRC, STAGE_SOURCE[stage])] + sorted(glob.glob(os.path.join(CSRC, "*.h")))
+    return sources_digest_files([STAGE_SOURCE[stage]])
+
+
+def sources_digest_files(srcs):
+    """Hash of the given csrc .hip files and every csrc header."""
+    files = [os.path.join(CSRC, f) for f in srcs] + sorted(glob.glob(os.path.join(CSRC, "*.h")))
     h = hashlib.sha256()
     for f in files:
         with open(f, "rb") as fh:
@@ -406,6 +443,98 @@ def traffic_markdown(fetch_csv, write_csv, wl, target):
     return "\n".join(lines), rec
 
 
+def label_ffn_dispatches(names):
+    """Call of FFN_CALLS that launched each library dispatch of an FFN-only run, given the dispatches'
+    demangled names in launch order; every pass must launch the same kernel sequence."""
+    bases = [kernel_base(n) for n in names]
+    lib = [i for i, b in enumerate(bases) if stage_of(b)]
+    labels = [c for c, n, _ in FFN_CALLS for _ in range(n)]
+    allowed = [a for _, n, a in FFN_CALLS for _ in range(n)]
+    per = len(labels)
+    if not lib or len(lib) % per:
+        raise SystemExit(f"{len(lib)} library dispatches: not a whole number of {per}-dispatch FFN passes")
+    out = {}
+    for j, i in enumerate(lib):
+        p = j % per
+        if stage_of(bases[i]) not in allowed[p] or bases[i] != bases[lib[p]]:
+            raise SystemExit(f"dispatch {j} ({bases[i]}) does not fit call {labels[p]} of an FFN pass")
+        out[i] = (labels[p], bases[i], p)
+    return out
+
+
+def ffn_stats_markdown(trace_csv):
+    """Markdown table of an FFN-only rocprofv3 --kernel-trace: per (call, kernel), calls and durations."""
+    rows = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Start_Timestamp"]))
+    lab = label_ffn_dispatches([r["Kernel_Name"] for r in rows])
+    per = {}
+    for i, (c, b, _) in lab.items():
+        per.setdefault((c, b), []).append((int(rows[i]["End_Timestamp"]) - int(rows[i]["Start_Timestamp"])) / 1e3)
+    order = {c: k for k, (c, _, _) in enumerate(FFN_CALLS)}
+    out = ["| call | kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|---|"]
+    for (c, b), v in sorted(per.items(), key=lambda kv: (order[kv[0][0]], kv[0][1])):
+        out.append(f"| {c} | `{b}` | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
+    return "\n".join(out)
+
+
+def ffn_traffic_markdown(fetch_csv, write_csv, wl):
+    """Per-call HBM bytes per launch of an FFN-only --profile-pass, scaled like traffic_markdown."""
+    def read(path, counter):
+        rows = sorted((r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter),
+                      key=lambda r: int(r["Dispatch_Id"]))
+        lab = label_ffn_dispatches([r["Kernel_Name"] for r in rows])
+        per, kern, calib = {}, {}, None
+        for i, r in enumerate(rows):
+            if i in lab:  # average each position of the pass over passes, then sum a call's positions
+                c, b, p = lab[i]
+                per.setdefault(c, {}).setdefault(p, []).append(float(r["Counter_Value"]))
+                kern.setdefault(c, set()).add(b)
+            elif "copyBuffer" in r["Kernel_Name"]:
+                calib = float(r["Counter_Value"])  # the last device copy is the 1 GiB calibration copy
+        return {c: sum(sum(v) / len(v) for v in d.values()) for c, d in per.items()}, kern, calib
+    fetch, kern, cf = read(fetch_csv, "FETCH_SIZE")
+    write, _, cw = read(write_csv, "WRITE_SIZE")
+    fs, ws = 1024 * 1024 / cf, 1024 * 1024 / cw
+    calls = {}
+    lines = ["| call | kernels | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes per launch (scaled) |",
+             "|---|---|---|---|---|"]
+    for c, _, stages in FFN_CALLS:
+        f, w, ks = fetch[c], write[c], sorted(kern[c])
+        b = f * 1024 * fs + w * 1024 * ws
+        srcs = sorted({STAGE_SOURCE[st] for st in stages})
+        calls[c] = {"kernels": ks, "fetch_kib": round(f, 1), "write_kib": round(w, 1),
+                    "bytes_per_launch": round(b), "sources": sources_digest_files(srcs)}
+        lines.append(f"| {c} | {', '.join('`' + k + '`' for k in ks)} | {f:.1f} | {w:.1f} | {b:.4g} |")
+    rec = {"workload": wl.name, "calibration": {"copy_bytes": 1 << 30, "fetch_kib": cf, "write_kib": cw,
+                                                "fetch_scale": round(fs, 4), "write_scale": round(ws, 4)},
+           "calls": calls}
+    return "\n".join(lines), rec
+
+
+def load_ffn_traffic(wl):
+    """HBM bytes per launch of each FFN call from profiles/traffic_<workload>_ffn.md, for the calls whose
+    kernels' sources still hash as they did when the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{wl.name}_ffn.md")
+    if not os.path.exists(path):
+        return {}
+    text = open(path).read()
+    rec = json.loads(text[text.index("```json") + 7:text.rindex("```")])
+    out = {}
+    for c, _, stages in FFN_CALLS:
+        r = rec["calls"].get(c)
+        if r and r["sources"] == sources_digest_files(sorted({STAGE_SOURCE[st] for st in stages})):
+            out[c] = r["bytes_per_launch"]
+    return out
+
+
+def cpu_sample_tokens(wl):
+    """Tokens per rank of the oracle's timed sample: the whole workload while its GEMM work is at most
+    the mid workload's (2*N*H*H' with N = 196608, H = 2048, H' = 1408; 10-20 s of float64 BLAS on 8-16
+    cores), else as many tokens as give that much work; 640 tokens per rank for routing-only workloads."""
+    if wl.Hp is None:
+        return max(1, min(wl.S, 640))
+    return max(1, min(wl.S, 196608 * 2048 * 1408 // (wl.H * wl.Hp) // (wl.R * wl.K)))
+
+
 def cpu_baseline(wl, seed, alpha, tokens_per_rank):
     """The oracle as it stands, on a bounded sample: the same routing recipe with S' tokens per rank and
     the workload's full E, B, H, H'; pairs/s = sampled pairs / oracle time of the whole step."""
@@ -443,6 +572,17 @@ def cpu_baseline(wl, seed, alpha, tokens_per_rank):
                       f"recipe with S={sw.S} tokens per rank ({sw.N} pairs), full E/B/H/H', float64; {t:.1f} s"}
 
 
+def calibration_copy():
+    """A plain copy kernel moving 1 GiB in and 1 GiB out, whose counters scale the traffic readings."""
+    import torch
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -465,8 +605,14 @@ def main():
     if args.stats_md:
         print(stats_markdown(args.stats_md))
         return
-    if args.traffic_md:
-        table, rec = traffic_markdown(args.traffic_md[0], args.traffic_md[1], wl, head_target)
+    if args.ffn_stats_md:
+        print(ffn_stats_markdown(args.ffn_stats_md))
+        return
+    if args.ffn_traffic_md or args.traffic_md:
+        if args.ffn_traffic_md:
+            table, rec = ffn_traffic_markdown(args.ffn_traffic_md[0], args.ffn_traffic_md[1], wl)
+        else:
+            table, rec = traffic_markdown(args.traffic_md[0], args.traffic_md[1], wl, head_target)
         print(table)
         print()
         print("```json")
@@ -488,6 +634,20 @@ def main():
         key_wl = WORKLOADS["mid_bwd"] if (args.workload == "mid" and target == 2.0) else wl
         return alpha_for(key_wl, args.seed, target)
 
+    if args.ffn_only:
+        if wl.Hp is None:
+            raise SystemExit("--ffn-only needs a workload with H'")
+        if args.profile_pass:
+            F, calls = make_ffn(wl, args.seed, alpha_of(head_target))
+            for _ in range(1 + args.steps):
+                for _, f in calls:
+                    f()
+            torch.cuda.synchronize()
+            calibration_copy()
+            log("profile pass done: FFN passes, then a 1 GiB copy")
+        else:
+            print(json.dumps({"ffn": time_ffn(wl, args.seed, alpha_of(head_target), args.steps, args.warmup)}))
+        return
     log(f"workload {wl.description}; building buffers")
     L = make_layer(wl, backward)
     if args.profile_pass:
@@ -498,12 +658,7 @@ def main():
             for _, f in stage_calls(L, backward) + (next_calls(L) if backward else []):
                 f()
         torch.cuda.synchronize()
-        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        src.fill_(1)
-        torch.cuda.synchronize()
-        dst.copy_(src)  # a plain copy kernel moving 1 GiB in and 1 GiB out
-        torch.cuda.synchronize()
+        calibration_copy()
         log("profile pass done: stages", [n for n, _ in stage_calls(L, backward)], "then a 1 GiB copy")
         return
     results = {}
@@ -552,7 +707,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
-        cpu = cpu_baseline(wl, args.seed, h["alpha"], tokens_per_rank=max(1, min(wl.S, 640)))
+        cpu = cpu_baseline(wl, args.seed, h["alpha"], tokens_per_rank=cpu_sample_tokens(wl))
 
     sweep = []
     for tgt in points:

@@ -1,0 +1,140 @@
+"""Host logic of bench.py, CPU only: the one-GPU refusal, kernel-name parsing and stage mapping, the
+per-call labelling of full-FFN profiles, and the counter scaling of the traffic summaries, on small
+synthetic rocprofv3 CSVs."""
+import csv
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+# demangled names as rocprofv3 prints them, one per library kernel an FFN pass launches
+NAMES = {
+    "plan_count": "void moonep::(anonymous namespace)::plan_count(moonep_dims, int const*, int*)",
+    "plan_scan": "void moonep::(anonymous namespace)::plan_scan(int*)",
+    "plan_solve": "void moonep::(anonymous namespace)::plan_solve(moonep_dims, int*)",
+    "plan_emit": "void moonep::(anonymous namespace)::plan_emit(moonep_dims, int const*, int*)",
+    "dispatch": "void moonep::(anonymous namespace)::dispatch_rows<unsigned int __vector(4)>(long, int, void const*)",
+    "prefetch": "void moonep::(anonymous namespace)::prefetch_slots<unsigned int __vector(4)>(long)",
+    "tiles": "moonep::(anonymous namespace)::ggemm_tiles(moonep_dims, int const*, int*)",
+    "fwd": "void moonep::fwd::(anonymous namespace)::ggemm_bf16<false>(moonep::fwd::GemmArgs)",
+    "dgrad": "void moonep::fwd::(anonymous namespace)::ggemm_bf16<true>(moonep::fwd::GemmArgs)",
+    "swiglu": "void moonep::(anonymous namespace)::swiglu_vec<unsigned short>(unsigned short const*, long, int)",
+    "swiglu_bwd": "void moonep::(anonymous namespace)::swiglu_bwd_vec<unsigned short>(unsigned short const*)",
+    "combine": "void moonep::(anonymous namespace)::combine_vec<8, 2, true>(long)",
+    "combine_bwd": "void moonep::(anonymous namespace)::combine_bwd_vec<8, 2, 4>(long)",
+    "dispatch_bwd": "void moonep::(anonymous namespace)::combine_vec<8, 2, false>(long)",
+    "wsched": "void moonep::wg::(anonymous namespace)::wgrad_schedule(moonep_dims, int*)",
+    "wgrad": "void moonep::wg::(anonymous namespace)::wgrad_bf16(moonep::wg::WArgs)",
+    "reduce": "void moonep::(anonymous namespace)::reduce_grad_kernel(long, float*)",
+}
+PASS = ["plan_count", "plan_scan", "plan_solve", "plan_emit", "dispatch", "prefetch", "prefetch",
+        "tiles", "fwd", "swiglu", "tiles", "fwd", "combine", "combine_bwd", "tiles", "dgrad", "wsched", "wgrad",
+        "swiglu_bwd", "tiles", "dgrad", "wsched", "wgrad", "dispatch_bwd", "reduce", "reduce"]
+TORCH = "void at::native::vectorized_elementwise_kernel<4, at::native::FillFunctor<float>>(int, float)"
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stdout
+
+
+@pytest.mark.parametrize("key,base,stage", [
+    ("fwd", "ggemm_bf16<false>", "group_gemm"), ("dgrad", "ggemm_bf16<true>", "dgrad"),
+    ("tiles", "ggemm_tiles", "group_gemm"), ("combine", "combine_vec<8, 2, true>", "combine"),
+    ("dispatch_bwd", "combine_vec<8, 2, false>", "dispatch_backward"), ("wgrad", "wgrad_bf16", "wgrad"),
+    ("dispatch", "dispatch_rows<unsigned int __vector(4)>", "dispatch"), ("swiglu_bwd",
+     "swiglu_bwd_vec<unsigned short>", "swiglu_backward"), ("plan_emit", "plan_emit", "plan"),
+])
+def test_kernel_base_and_stage(key, base, stage):
+    assert bench.kernel_base(NAMES[key]) == base
+    assert bench.stage_of(base) == stage
+
+
+def test_torch_kernels_have_no_stage():
+    assert bench.stage_of(bench.kernel_base(TORCH)) is None
+
+
+def test_ffn_call_table_matches_the_pass():
+    assert sum(n for _, n, _ in bench.FFN_CALLS) == len(PASS)
+
+
+def test_ffn_labels_follow_the_pass_and_skip_foreign_kernels():
+    names = [TORCH] + [NAMES[k] for k in PASS] + [TORCH, TORCH] + [NAMES[k] for k in PASS]
+    lab = bench.label_ffn_dispatches(names)
+    assert len(lab) == 2 * len(PASS) and 0 not in lab
+    calls = [lab[i][0] for i in sorted(lab)]
+    # the two forward GEMMs and the two dgrads are told apart by their place in the pass
+    fwd = [c for i, c in zip(sorted(lab), calls) if lab[i][1] == "ggemm_bf16<false>"]
+    assert fwd == ["gemm_gate_up", "gemm_down"] * 2
+    dg = [c for i, c in zip(sorted(lab), calls) if lab[i][1] == "ggemm_bf16<true>"]
+    assert dg == ["dgrad_down", "dgrad_gate_up"] * 2
+    assert calls[:4] == ["plan"] * 4 and calls[-2:] == ["reduce_grad"] * 2
+
+
+def test_ffn_labels_reject_a_broken_pass():
+    bad = [NAMES[k] for k in PASS]
+    bad[9], bad[13] = bad[13], bad[9]  # swiglu where combine backward should be
+    with pytest.raises(SystemExit):
+        bench.label_ffn_dispatches([NAMES[k] for k in PASS] + bad)
+    with pytest.raises(SystemExit):
+        bench.label_ffn_dispatches([NAMES[k] for k in PASS[:-1]])
+
+
+def _trace(path, names, dur):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        t = 1000
+        for n, d in zip(names, dur):
+            w.writerow({"Kernel_Name": n, "Start_Timestamp": t, "End_Timestamp": t + d})
+            t += d + 10
+
+
+def test_ffn_stats_table_averages_per_call(tmp_path):
+    names = [NAMES[k] for k in PASS] * 3
+    dur = []
+    for p in range(3):
+        for i, k in enumerate(PASS):
+            gemm = k == "fwd"
+            first = PASS.index("fwd") == i
+            dur.append((2000 if first else 1000) * (p + 1) if gemm else 100)
+    path = str(tmp_path / "trace.csv")
+    _trace(path, names, dur)
+    md = bench.ffn_stats_markdown(path)
+    rows = {tuple(c.strip(" `") for c in line.split("|")[1:3]): line for line in md.splitlines()[2:]}
+    assert "| 3 | 4.00 | 2.00 | 6.00 |" in rows[("gemm_gate_up", "ggemm_bf16<false>")]
+    assert "| 3 | 2.00 | 1.00 | 3.00 |" in rows[("gemm_down", "ggemm_bf16<false>")]
+    assert "| 6 | 0.10 |" in rows[("prefetch", "prefetch_slots<unsigned int __vector(4)>")]
+
+
+def _counters(path, counter, names, values):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for i, (n, v) in enumerate(zip(names, values)):
+            w.writerow({"Dispatch_Id": i + 1, "Kernel_Name": n, "Counter_Name": counter, "Counter_Value": v})
+
+
+def test_ffn_traffic_sums_a_calls_dispatches_and_scales_by_the_copy(tmp_path):
+    copy = "__amd_rocclr_copyBuffer"
+    names = [NAMES[k] for k in PASS] * 2 + [copy]
+    # fetch counter reads half of the copy's 1 GiB, write counter all of it
+    fv = [10.0] * (2 * len(PASS)) + [524288.0]
+    wv = [3.0] * (2 * len(PASS)) + [1048576.0]
+    f, w = str(tmp_path / "f.csv"), str(tmp_path / "w.csv")
+    _counters(f, "FETCH_SIZE", names, fv)
+    _counters(w, "WRITE_SIZE", names, wv)
+    from synthetic import WORKLOADS
+    _, rec = bench.ffn_traffic_markdown(f, w, WORKLOADS["mid_fwd"])
+    assert rec["calibration"]["fetch_scale"] == 2.0 and rec["calibration"]["write_scale"] == 1.0
+    # reduce_grad launches two kernels per pass: 2 x (10 KiB x 2 + 3 KiB) per call
+    assert rec["calls"]["reduce_grad"]["bytes_per_launch"] == 2 * (10 * 1024 * 2 + 3 * 1024)
+    assert rec["calls"]["swiglu"]["bytes_per_launch"] == 10 * 1024 * 2 + 3 * 1024
+    assert rec["calls"]["plan"]["bytes_per_launch"] == 4 * (10 * 1024 * 2 + 3 * 1024)
