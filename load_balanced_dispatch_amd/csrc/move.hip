@@ -7,8 +7,8 @@
 //   dispatch    one wave per 64-element piece of a token's row: read once into
 //               registers, stored K times (fused permute into the expert-grouped buffer).
 //   prefetch    persistent blocks copy every used slot's [H,Hp] expert matrix.
-//   combine     one thread per 16 bytes of input row: K gathers (non-temporal: Yp is read
-//               once), fp32 FMA in k order.
+//   combine     one thread per 16 bytes of input row: K gathers issued together
+//               (non-temporal: Yp is read once), fp32 FMA in k order.
 //   reduce_grad persistent blocks fold each expert's slot gradients (ranks in
 //               ascending order) into the home gradient and zero the slots.
 #include "block_scan.h"
@@ -22,9 +22,10 @@ namespace {
 constexpr int kDispatchThreads = 256;
 
 // One wave per 64-element piece of a token's row (1 KB with 16-byte elements): each lane reads its
-// element once and stores it K times with non-temporal stores.  Many short waves keep more rows in
-// flight than one wave walking a whole row, which measured ~9% faster on the 4 KB rows of the mid
-// workload.
+// element once and stores it K times.  Many short waves keep more rows in flight than one wave
+// walking a whole row, which measured ~9% faster on the 4 KB rows of the mid workload.  Ordinary
+// stores measured 8% faster than non-temporal ones here; issuing a token's K stores back to back
+// (destinations read first) measured no faster than this loop.
 template <typename V>
 __global__ __launch_bounds__(kDispatchThreads) void dispatch_rows(const V* __restrict__ X,
                                                                   const int32_t* __restrict__ dest,
@@ -38,7 +39,7 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_rows(const V* __res
   const int32_t* dk = dest + tok * K;
   for (int k = 0; k < K; ++k) {
     const int32_t d = dk[k];
-    if (d >= 0) __builtin_nontemporal_store(x, Xp + (int64_t)d * nvec + v);
+    if (d >= 0) Xp[(int64_t)d * nvec + v] = x;
   }
 }
 
@@ -110,38 +111,60 @@ struct InVec<4> {  // 4 f32
 };
 
 constexpr int kCombineThreads = 256;
+constexpr int kBatch = 8;  // gathers a combine thread keeps in flight
 
 // VEC elements of 16 bytes per thread; ESZ = element bytes of Yp.  With GATED false every gate is 1
 // and gates is not read (the gradient of dispatch: dX[r,s] = sum_k dXp[dest]); fma(1, y, acc)
-// rounds as y + acc.
-template <int VEC, int ESZ, bool GATED>
+// rounds as y + acc.  The gathers of a batch of k are all issued before the first is used, so a
+// thread keeps up to kBatch 16-byte loads in flight; they are summed in ascending k as before.  A
+// dropped pair (dest < 0) loads row 0 and is discarded by a select rather than a branch, which
+// would make the compiler wait for each gather in turn.  IDX is the index type of the thread's item
+// (32 bits when tokens * D / VEC fits); KC > 0 fixes K at compile time (KC = 0: K from the call).
+template <int VEC, int ESZ, bool GATED, typename IDX, int KC>
 __global__ __launch_bounds__(kCombineThreads) void combine_vec(const char* __restrict__ Yp,
                                                                const int32_t* __restrict__ dest,
                                                                const float* __restrict__ gates,
-                                                               float* __restrict__ out, int64_t tokens, int K,
+                                                               float* __restrict__ out, int64_t tokens, int K_arg,
                                                                int D) {
+  const int K = KC > 0 ? KC : K_arg;
   const int nchunk = D / VEC;
-  const int64_t item = (int64_t)blockIdx.x * kCombineThreads + threadIdx.x;
-  if (item >= tokens * nchunk) return;
-  const int64_t tok = item / nchunk;
-  const int c = (int)(item % nchunk);
+  const IDX item = (IDX)blockIdx.x * kCombineThreads + threadIdx.x;
+  if ((int64_t)item >= tokens * nchunk) return;
+  const IDX tq = item / (IDX)nchunk;
+  const int c = (int)(item - tq * (IDX)nchunk);
+  const int64_t tok = (int64_t)tq;
+  const int32_t* dk = dest + tok * K;
+  const float* gk = GATED ? gates + tok * K : nullptr;
   float acc[VEC];
 #pragma unroll
   for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
-  for (int k = 0; k < K; ++k) {
-    const int32_t d = dest[tok * K + k];
-    if (d < 0) continue;
-    const float g = GATED ? gates[tok * K + k] : 1.f;
-    float y[VEC];
-    InVec<VEC>::load(Yp + ((int64_t)d * D + (int64_t)c * VEC) * ESZ, y);
+  for (int k0 = 0; k0 < K; k0 += kBatch) {
+    int32_t d[kBatch];
+    float g[kBatch], y[kBatch][VEC];
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) acc[i] = __builtin_fmaf(g, y[i], acc[i]);
+    for (int u = 0; u < kBatch; ++u) {
+      d[u] = k0 + u < K ? dk[k0 + u] : -1;
+      g[u] = GATED && k0 + u < K ? gk[k0 + u] : 1.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (k0 + u < K) InVec<VEC>::load(Yp + ((int64_t)max(d[u], 0) * D + (int64_t)c * VEC) * ESZ, y[u]);
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (k0 + u < K) {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+          const float f = __builtin_fmaf(g[u], y[u][i], acc[i]);
+          acc[i] = d[u] >= 0 ? f : acc[i];
+        }
+      }
   }
   f32x4* o = reinterpret_cast<f32x4*>(out + tok * D + (int64_t)c * VEC);
 #pragma unroll
   for (int i = 0; i < VEC / 4; ++i) {
-    f32x4 q = {acc[4 * i], acc[4 * i + 1], acc[4 * i + 2], acc[4 * i + 3]};
-    __builtin_nontemporal_store(q, o + i);
+    const f32x4 q = {acc[4 * i], acc[4 * i + 1], acc[4 * i + 2], acc[4 * i + 3]};
+    if (GATED) o[i] = q;
+    else __builtin_nontemporal_store(q, o + i);
   }
 }
 
@@ -468,6 +491,37 @@ extern "C" int moonep_prefetch(moonep_dims d, int32_t H, int32_t Hp, moonep_dtyp
 
 namespace {
 
+template <int VEC, int ESZ, bool GATED, int KC>
+void combine_vec_k(unsigned grid, hipStream_t s, const char* y, const int32_t* dest, const float* gates, float* out,
+                   int64_t tokens, int K, int D) {
+  hipLaunchKernelGGL((combine_vec<VEC, ESZ, GATED, uint32_t, KC>), dim3(grid), dim3(kCombineThreads), 0, s, y, dest,
+                     gates, out, tokens, K, D);
+}
+
+// K up to kBatch gets its own instantiation (the batch then has no branches); 64-bit item indices
+// or a larger K take the kernel with K from the call.
+template <int VEC, int ESZ, bool GATED>
+void combine_vec_launch(bool idx32, int K, unsigned grid, hipStream_t s, const char* y, const int32_t* dest,
+                        const float* gates, float* out, int64_t tokens, int D) {
+  static_assert(kBatch == 8, "one case per K up to kBatch");
+  if (!idx32) {
+    hipLaunchKernelGGL((combine_vec<VEC, ESZ, GATED, int64_t, 0>), dim3(grid), dim3(kCombineThreads), 0, s, y, dest,
+                       gates, out, tokens, K, D);
+    return;
+  }
+  switch (K) {
+    case 1: combine_vec_k<VEC, ESZ, GATED, 1>(grid, s, y, dest, gates, out, tokens, K, D); break;
+    case 2: combine_vec_k<VEC, ESZ, GATED, 2>(grid, s, y, dest, gates, out, tokens, K, D); break;
+    case 3: combine_vec_k<VEC, ESZ, GATED, 3>(grid, s, y, dest, gates, out, tokens, K, D); break;
+    case 4: combine_vec_k<VEC, ESZ, GATED, 4>(grid, s, y, dest, gates, out, tokens, K, D); break;
+    case 5: combine_vec_k<VEC, ESZ, GATED, 5>(grid, s, y, dest, gates, out, tokens, K, D); break;
+    case 6: combine_vec_k<VEC, ESZ, GATED, 6>(grid, s, y, dest, gates, out, tokens, K, D); break;
+    case 7: combine_vec_k<VEC, ESZ, GATED, 7>(grid, s, y, dest, gates, out, tokens, K, D); break;
+    case 8: combine_vec_k<VEC, ESZ, GATED, 8>(grid, s, y, dest, gates, out, tokens, K, D); break;
+    default: combine_vec_k<VEC, ESZ, GATED, 0>(grid, s, y, dest, gates, out, tokens, K, D); break;
+  }
+}
+
 // combine (GATED) and dispatch backward (unit gates)
 template <bool GATED>
 int combine_launch(const char* name, moonep_dims d, int32_t D, moonep_dtype t, const void* Yp,
@@ -476,13 +530,14 @@ int combine_launch(const char* name, moonep_dims d, int32_t D, moonep_dtype t, c
   clear_stale_error();
   const int vec = t == MOONEP_BF16 ? 8 : 4;
   if (D % vec == 0 && aligned16(Yp) && aligned16(out)) {
-    const unsigned grid = ceil_div_u(tokens * (D / vec), kCombineThreads);
+    const int64_t items = tokens * (D / vec);
+    const unsigned grid = ceil_div_u(items, kCombineThreads);
+    const bool idx32 = (int64_t)grid * kCombineThreads < (int64_t(1) << 32);
+    const char* y = static_cast<const char*>(Yp);
     if (t == MOONEP_BF16)
-      hipLaunchKernelGGL((combine_vec<8, 2, GATED>), dim3(grid), dim3(kCombineThreads), 0, s,
-                         static_cast<const char*>(Yp), dest_idx, gates, out, tokens, d.K, (int)D);
+      combine_vec_launch<8, 2, GATED>(idx32, d.K, grid, s, y, dest_idx, gates, out, tokens, (int)D);
     else
-      hipLaunchKernelGGL((combine_vec<4, 4, GATED>), dim3(grid), dim3(kCombineThreads), 0, s,
-                         static_cast<const char*>(Yp), dest_idx, gates, out, tokens, d.K, (int)D);
+      combine_vec_launch<4, 4, GATED>(idx32, d.K, grid, s, y, dest_idx, gates, out, tokens, (int)D);
   } else {
     const unsigned grid = ceil_div_u(tokens * D, kCombineThreads);
     if (t == MOONEP_BF16)

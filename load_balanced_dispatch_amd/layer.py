@@ -106,11 +106,14 @@ class MoeLayer:
 
     def forward(self, stream=None):
         self.plan(stream)
+        if self.Hp is None:
+            self.dispatch(stream)
+            return
+        # the weight prefetch needs only the plan, so it runs while (here: before) tokens dispatch
+        self.prefetch(stream)
         self.dispatch(stream)
-        if self.Hp is not None:
-            self.prefetch(stream)
-            self.group_gemm(stream)
-            self.combine(stream)
+        self.group_gemm(stream)
+        self.combine(stream)
 
     def backward(self, stream=None):
         self.wgrad(stream)
@@ -181,11 +184,11 @@ class MoeFFN:
         return [
             ("plan", lambda: L.moonep_plan(d, self.topk_idx, self.expert_counts, self.maxvio, self.cu_seqlens,
                                            sl(self.slot_expert), self.dest_idx, None, self.stats, self.ws_plan)),
-            ("dispatch", lambda: L.moonep_dispatch(d, H, self.X, self.dest_idx, self.Xp)),
             ("prefetch", lambda: (L.moonep_prefetch(d, H, 2 * Hp, self.W_gu_home, sl(self.slot_expert),
                                                     sl(self.W_gu_slots)),
                                   L.moonep_prefetch(d, Hp, H, self.W_down_home, sl(self.slot_expert),
                                                     sl(self.W_down_slots)))),
+            ("dispatch", lambda: L.moonep_dispatch(d, H, self.X, self.dest_idx, self.Xp)),
             ("gemm_gate_up", lambda: L.moonep_group_gemm(d, H, 2 * Hp, self.Xp, self.W_gu_home, sl(self.W_gu_slots),
                                                          self.cu_seqlens, self.Ygu, self.ws_gemm)),
             ("swiglu", lambda: L.moonep_swiglu(d, Hp, self.Ygu, self.A)),

@@ -25,14 +25,14 @@ NAMES = {
     "dgrad": "void moonep::fwd::(anonymous namespace)::ggemm_bf16<true>(moonep::fwd::GemmArgs)",
     "swiglu": "void moonep::(anonymous namespace)::swiglu_vec<unsigned short>(unsigned short const*, long, int)",
     "swiglu_bwd": "void moonep::(anonymous namespace)::swiglu_bwd_vec<unsigned short>(unsigned short const*)",
-    "combine": "void moonep::(anonymous namespace)::combine_vec<8, 2, true>(long)",
+    "combine": "void moonep::(anonymous namespace)::combine_vec<8, 2, true, unsigned int, 6>(long)",
     "combine_bwd": "void moonep::(anonymous namespace)::combine_bwd_vec<8, 2, 4>(long)",
-    "dispatch_bwd": "void moonep::(anonymous namespace)::combine_vec<8, 2, false>(long)",
+    "dispatch_bwd": "void moonep::(anonymous namespace)::combine_vec<8, 2, false, unsigned int, 6>(long)",
     "wsched": "void moonep::wg::(anonymous namespace)::wgrad_schedule(moonep_dims, int*)",
     "wgrad": "void moonep::wg::(anonymous namespace)::wgrad_bf16(moonep::wg::WArgs)",
     "reduce": "void moonep::(anonymous namespace)::reduce_grad_kernel(long, float*)",
 }
-PASS = ["plan_count", "plan_scan", "plan_solve", "plan_emit", "dispatch", "prefetch", "prefetch",
+PASS = ["plan_count", "plan_scan", "plan_solve", "plan_emit", "prefetch", "prefetch", "dispatch",
         "tiles", "fwd", "swiglu", "tiles", "fwd", "combine", "combine_bwd", "tiles", "dgrad", "wsched", "wgrad",
         "swiglu_bwd", "tiles", "dgrad", "wsched", "wgrad", "dispatch_bwd", "reduce", "reduce"]
 TORCH = "void at::native::vectorized_elementwise_kernel<4, at::native::FillFunctor<float>>(int, float)"
@@ -47,8 +47,8 @@ def test_more_than_one_gpu_is_refused():
 
 @pytest.mark.parametrize("key,base,stage", [
     ("fwd", "ggemm_bf16<false>", "group_gemm"), ("dgrad", "ggemm_bf16<true>", "dgrad"),
-    ("tiles", "ggemm_tiles", "group_gemm"), ("combine", "combine_vec<8, 2, true>", "combine"),
-    ("dispatch_bwd", "combine_vec<8, 2, false>", "dispatch_backward"), ("wgrad", "wgrad_bf16", "wgrad"),
+    ("tiles", "ggemm_tiles", "group_gemm"), ("combine", "combine_vec<8, 2, true, unsigned int, 6>", "combine"),
+    ("dispatch_bwd", "combine_vec<8, 2, false, unsigned int, 6>", "dispatch_backward"), ("wgrad", "wgrad_bf16", "wgrad"),
     ("dispatch", "dispatch_rows<unsigned int __vector(4)>", "dispatch"), ("swiglu_bwd",
      "swiglu_bwd_vec<unsigned short>", "swiglu_backward"), ("plan_emit", "plan_emit", "plan"),
 ])
@@ -59,6 +59,15 @@ def test_kernel_base_and_stage(key, base, stage):
 
 def test_torch_kernels_have_no_stage():
     assert bench.stage_of(bench.kernel_base(TORCH)) is None
+
+
+@pytest.mark.parametrize("base,stage", [
+    ("combine_vec<4, 4, true, long, 0>", "combine"), ("combine_scalar<unsigned short, true>", "combine"),
+    ("combine_vec<8, 2, false, long, 0>", "dispatch_backward"), ("combine_scalar<float, false>", "dispatch_backward"),
+    ("combine_bwd_vec<8, 2, 4>", "combine_backward"), ("combine_bwd_scalar<float>", "combine_backward"),
+])
+def test_combine_instances_map_to_their_stage(base, stage):
+    assert bench.stage_of(base) == stage
 
 
 def test_ffn_call_table_matches_the_pass():

@@ -196,6 +196,7 @@ def test_prefetch_bit_exact_and_unused_slots_untouched(m, dtype, H, Hp):
     (torch.bfloat16, 2, 4, 2, 300, 2, 192, 256),    # MFMA path: 2+ M tiles per group, partial tiles, 2 N tiles
     (torch.bfloat16, 4, 16, 4, 160, 3, 128, 128),   # MFMA path, many small groups and slots
     (torch.bfloat16, 3, 6, 0, 200, 2, 64, 384),     # MFMA path, no slots, direct reads
+    (torch.bfloat16, 2, 4, 2, 200, 2, 128, 320),    # MFMA path, 64-wide last n tile (narrow wave layout)
     (torch.bfloat16, 2, 4, 1, 50, 2, 40, 72),       # generic bf16 path (H % 64 != 0)
     (torch.float32, 4, 16, 4, 64, 2, 128, 256),     # tiny workload shape, float32
     (torch.float32, 2, 6, 1, 37, 3, 33, 65),        # float32, ragged everything
