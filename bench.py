@@ -575,6 +575,37 @@ def cpu_baseline(wl, seed, alpha, tokens_per_rank):
                       f"recipe with S={sw.S} tokens per rank ({sw.N} pairs), full E/B/H/H', float64; {t:.1f} s"}
 
 
+def hot_rank_factor(idx, wl):
+    """What an unbalanced EP would wait for: the most loaded rank's pairs (the pairs routed to its
+    E/R home experts) over the P = S*K pairs every rank holds after balancing."""
+    import numpy as np
+    counts = np.bincount(np.asarray(idx).reshape(-1), minlength=wl.E)
+    per_rank = counts.reshape(wl.R, wl.E // wl.R).sum(axis=1)
+    return float(per_rank.max()) / float(wl.S * wl.K)
+
+
+def copy_ceiling_gbs(reps=5):
+    """Achievable HBM rate of a plain device copy (torch's copy kernel, 1 GiB read + 1 GiB written),
+    timed with events on the current stream: the measured ceiling the HBM-bound stages are also
+    compared against."""
+    import torch
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * (1 << 30) / (ms * 1e-3) / 1e9
+
+
 def calibration_copy():
     """A plain copy kernel moving 1 GiB in and 1 GiB out, whose counters scale the traffic readings."""
     import torch
@@ -675,7 +706,8 @@ def main():
         stats = L.stats.cpu().numpy()
         slots = L.slot_expert.cpu().numpy()
         results[tgt] = dict(alpha=alpha, maxvio=float(L.maxvio.item()), ms=ms, stages=stages,
-                            stats=stats.tolist(), slots=slots, maxvio_host=measured_maxvio(idx, wl.E))
+                            stats=stats.tolist(), slots=slots, maxvio_host=measured_maxvio(idx, wl.E),
+                            hot_rank=hot_rank_factor(idx, wl))
         log(f"maxvio target {tgt}: measured {results[tgt]['maxvio']:.3f}, {ms:.3f} ms/step, stages {stages}")
 
     h = results[head_target]
@@ -718,8 +750,23 @@ def main():
         fwd = sum(r["stages"].get(n, 0.0) for n in ("plan", "dispatch", "prefetch", "group_gemm", "combine"))
         sweep.append({"maxvio_target": tgt, "maxvio": round(r["maxvio"], 4), "ms_per_step": round(r["ms"], 4),
                       "forward_ms": round(fwd, 4), "copies_slotted_direct": r["stats"][:3],
+                      "hot_rank_factor": round(r["hot_rank"], 4),
                       "stages_ms": {k: round(v, 4) for k, v in r["stages"].items()}})
     sweep.sort(key=lambda x: (x["maxvio_target"] is None, x["maxvio_target"]))
+    flat = None
+    if len(sweep) > 1:  # every point against the lowest-maxvio point: within +-10% is flat
+        f0, s0 = sweep[0]["forward_ms"], sweep[0]["ms_per_step"]
+        fr = [round(x["forward_ms"] / f0 - 1, 4) for x in sweep]
+        sr = [round(x["ms_per_step"] / s0 - 1, 4) for x in sweep]
+        flat = {"reference_maxvio": sweep[0]["maxvio"], "forward_rel": fr, "step_rel": sr,
+                "forward_within_10pct": all(abs(v) <= 0.10 for v in fr),
+                "step_within_10pct": all(abs(v) <= 0.10 for v in sr)}
+
+    log("timing a plain 1 GiB device copy (measured HBM ceiling)")
+    copy_gbs = copy_ceiling_gbs()
+    for entry in list(rooflines.values()) + [roofline] + [v for k, v in (next_rows or {}).items() if k != "ffn"]:
+        if entry.get("unit") == "GB/s":
+            entry["frac_of_copy"] = round(entry["achieved"] / copy_gbs, 4)
     line = {
         "metric": "token-expert pairs/s planned+dispatched; group-GEMM TFLOP/s; reduce_grad GB/s",
         "value": wl.N / (h["ms"] * 1e-3),
@@ -739,7 +786,11 @@ def main():
         "rooflines": rooflines,
         "next_rows": next_rows,
         "cpu_baseline": cpu,
+        "ceilings": {"copy_GBs": round(copy_gbs, 1),
+                     "note": "torch device copy of 1 GiB (read + write) on this GPU, HIP events; each GB/s "
+                             "stage's frac_of_copy is its achieved rate over this"},
         "sweep": sweep,
+        "sweep_flatness": flat,
     }
     print(json.dumps(line), flush=True)
 

@@ -69,9 +69,14 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Workgroup barrier that does not drain outstanding loads (unlike __syncthreads, whose fence waits
-// for every memory operation); LDS visibility of the DMA'd stage is ensured by wait_vmcnt first.
+// Workgroup barrier that does not drain outstanding global loads (unlike __syncthreads, whose fence
+// waits for every memory operation); LDS visibility of the DMA'd stage is ensured by wait_vmcnt
+// first.  It does drain this wave's LDS reads, so no ring slot is refilled under a pending read.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Barrier that leaves this wave's LDS reads in flight: for the one after a ping-pong memory phase
+// whose slot no wave refills before the next barrier.
+__device__ __forceinline__ void plain_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // Row of accumulator element v for lane l inside a 32x32 tile.
 __device__ __forceinline__ int acc_row(int v, int lane) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }

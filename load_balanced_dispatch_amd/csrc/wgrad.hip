@@ -308,7 +308,7 @@ __global__ __launch_bounds__(512, 1) void wgrad_bf16(const uint16_t* __restrict_
       for (int t = 0; t < KT; ++t) {
         even_barrier(t);
         mem(t);
-        lds_barrier();
+        plain_barrier();  // slot t is next refilled in phase 2t + 2, after comp() has consumed these reads
         comp();
       }
       even_barrier(KT);

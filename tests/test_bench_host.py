@@ -18,7 +18,7 @@ NAMES = {
     "plan_scan": "void moonep::(anonymous namespace)::plan_scan(int*)",
     "plan_solve": "void moonep::(anonymous namespace)::plan_solve(moonep_dims, int*)",
     "plan_emit": "void moonep::(anonymous namespace)::plan_emit(moonep_dims, int const*, int*)",
-    "dispatch": "void moonep::(anonymous namespace)::dispatch_rows<unsigned int __vector(4)>(long, int, void const*)",
+    "dispatch": "void moonep::(anonymous namespace)::dispatch_rows<unsigned int __vector(4), false>(long, int, void const*)",
     "prefetch": "void moonep::(anonymous namespace)::prefetch_slots<unsigned int __vector(4)>(long)",
     "tiles": "moonep::(anonymous namespace)::ggemm_tiles(moonep_dims, int const*, int*)",
     "fwd": "void moonep::fwd::(anonymous namespace)::ggemm_bf16<false>(moonep::fwd::GemmArgs)",
@@ -49,7 +49,7 @@ def test_more_than_one_gpu_is_refused():
     ("fwd", "ggemm_bf16<false>", "group_gemm"), ("dgrad", "ggemm_bf16<true>", "dgrad"),
     ("tiles", "ggemm_tiles", "group_gemm"), ("combine", "combine_vec<8, 2, true, unsigned int, 6>", "combine"),
     ("dispatch_bwd", "combine_vec<8, 2, false, unsigned int, 6>", "dispatch_backward"), ("wgrad", "wgrad_bf16", "wgrad"),
-    ("dispatch", "dispatch_rows<unsigned int __vector(4)>", "dispatch"), ("swiglu_bwd",
+    ("dispatch", "dispatch_rows<unsigned int __vector(4), false>", "dispatch"), ("swiglu_bwd",
      "swiglu_bwd_vec<unsigned short>", "swiglu_backward"), ("plan_emit", "plan_emit", "plan"),
 ])
 def test_kernel_base_and_stage(key, base, stage):
@@ -147,3 +147,16 @@ def test_ffn_traffic_sums_a_calls_dispatches_and_scales_by_the_copy(tmp_path):
     assert rec["calls"]["reduce_grad"]["bytes_per_launch"] == 2 * (10 * 1024 * 2 + 3 * 1024)
     assert rec["calls"]["swiglu"]["bytes_per_launch"] == 10 * 1024 * 2 + 3 * 1024
     assert rec["calls"]["plan"]["bytes_per_launch"] == 4 * (10 * 1024 * 2 + 3 * 1024)
+
+
+def test_hot_rank_factor_extremes():
+    import numpy as np
+    from synthetic import WORKLOADS
+    wl = WORKLOADS["mid_fwd"].with_dims(S=16)
+    per = wl.E // wl.R
+    # every token of every rank routed to rank 0's home experts: that rank would hold R times P
+    idx = np.tile(np.arange(wl.K) % per, (wl.R, wl.S, 1))
+    assert bench.hot_rank_factor(idx, wl) == wl.R
+    # each rank's pairs spread evenly over all ranks' experts: every rank holds exactly P
+    flat = (np.arange(wl.R * wl.S * wl.K) % wl.E).reshape(wl.R, wl.S, wl.K)
+    assert bench.hot_rank_factor(flat, wl) == 1.0
