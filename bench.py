@@ -584,10 +584,10 @@ def hot_rank_factor(idx, wl):
     return float(per_rank.max()) / float(wl.S * wl.K)
 
 
-def copy_ceiling_gbs(reps=5):
-    """Achievable HBM rate of a plain device copy (torch's copy kernel, 1 GiB read + 1 GiB written),
-    timed with events on the current stream: the measured ceiling the HBM-bound stages are also
-    compared against."""
+def runtime_copy_gbs(reps=5):
+    """HBM rate of the HIP runtime's own device-to-device copy (torch's copy_ of 1 GiB: 1 GiB read,
+    1 GiB written), timed with events on the current stream.  A reference point, not a ceiling: a
+    one-shot copy kernel with one 16-byte vector per thread measured about 6.5 TB/s on this GPU."""
     import torch
     src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
@@ -762,11 +762,11 @@ def main():
                 "forward_within_10pct": all(abs(v) <= 0.10 for v in fr),
                 "step_within_10pct": all(abs(v) <= 0.10 for v in sr)}
 
-    log("timing a plain 1 GiB device copy (measured HBM ceiling)")
-    copy_gbs = copy_ceiling_gbs()
+    log("timing the runtime's 1 GiB device copy (reference rate)")
+    copy_gbs = runtime_copy_gbs()
     for entry in list(rooflines.values()) + [roofline] + [v for k, v in (next_rows or {}).items() if k != "ffn"]:
         if entry.get("unit") == "GB/s":
-            entry["frac_of_copy"] = round(entry["achieved"] / copy_gbs, 4)
+            entry["frac_of_runtime_copy"] = round(entry["achieved"] / copy_gbs, 4)
     line = {
         "metric": "token-expert pairs/s planned+dispatched; group-GEMM TFLOP/s; reduce_grad GB/s",
         "value": wl.N / (h["ms"] * 1e-3),
@@ -786,9 +786,11 @@ def main():
         "rooflines": rooflines,
         "next_rows": next_rows,
         "cpu_baseline": cpu,
-        "ceilings": {"copy_GBs": round(copy_gbs, 1),
-                     "note": "torch device copy of 1 GiB (read + write) on this GPU, HIP events; each GB/s "
-                             "stage's frac_of_copy is its achieved rate over this"},
+        "reference_rates": {"runtime_copy_GBs": round(copy_gbs, 1),
+                            "note": "the HIP runtime's device copy of 1 GiB (read + write), HIP events; a GB/s "
+                                    "stage's frac_of_runtime_copy is its rate over this (above 1: faster than "
+                                    "the runtime's copy). A one-shot 16-byte-per-thread copy kernel measured "
+                                    "about 6.5 TB/s (81% of 8 TB/s), the practical HBM ceiling."},
         "sweep": sweep,
         "sweep_flatness": flat,
     }
