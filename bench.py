@@ -620,7 +620,7 @@ def calibration_copy():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; multi-GPU runs are not part of it",
+        print(json.dumps({"error": "this benchmark runs on one GPU only; more than one GPU is not supported",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     from synthetic import WORKLOADS
