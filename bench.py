@@ -606,6 +606,34 @@ def runtime_copy_gbs(reps=5):
     return 2 * (1 << 30) / (ms * 1e-3) / 1e9
 
 
+def vendor_gemm_tflops(wl, reps=5):
+    """The vendor BLAS (hipBLASLt via torch.matmul, bf16) on the group GEMM's FLOPs: R dense GEMMs of
+    [P, H] x [H, H'] (forward shape) and of [H, P] x [P, H'] (the weight-gradient shape), all
+    operands contiguous 2-D tensors, timed with events.  Context for the MFMA fraction: the same work
+    with one weight per P = S*K rows, an easier reuse pattern than the ragged groups."""
+    import torch
+    P, H, Hp, R = wl.S * wl.K, wl.H, wl.Hp, wl.R
+    g = torch.Generator(device="cuda").manual_seed(1)
+    out = {}
+    for name, (m, k, n) in (("fwd", (P, H, Hp)), ("wgrad", (H, P, Hp))):
+        a = torch.randn((m, k), device="cuda", dtype=torch.bfloat16, generator=g)
+        b = torch.randn((k, n), device="cuda", dtype=torch.bfloat16, generator=g)
+        for _ in range(2):
+            torch.matmul(a, b)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps * R):
+            torch.matmul(a, b)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[name] = 2.0 * R * m * k * n / (ms * 1e-3) / 1e12
+        del a, b
+    torch.cuda.empty_cache()
+    return out
+
+
 def calibration_copy():
     """A plain copy kernel moving 1 GiB in and 1 GiB out, whose counters scale the traffic readings."""
     import torch
@@ -762,8 +790,14 @@ def main():
                 "forward_within_10pct": all(abs(v) <= 0.10 for v in fr),
                 "step_within_10pct": all(abs(v) <= 0.10 for v in sr)}
 
-    log("timing the runtime's 1 GiB device copy (reference rate)")
+    log("timing the runtime's 1 GiB device copy and the vendor GEMM (reference rates)")
     copy_gbs = runtime_copy_gbs()
+    vendor = vendor_gemm_tflops(wl) if (wl.Hp is not None and wl.dtype == "bf16") else None
+    if vendor:
+        for n, key in (("group_gemm", "fwd"), ("dgrad", "fwd"), ("wgrad", "wgrad")):
+            for entry in [rooflines.get(n), (next_rows or {}).get(n)] + ([roofline] if roofline.get("stage") == n else []):
+                if entry:
+                    entry["frac_of_vendor_gemm"] = round(entry["achieved"] / vendor[key], 4)
     for entry in list(rooflines.values()) + [roofline] + [v for k, v in (next_rows or {}).items() if k != "ffn"]:
         if entry.get("unit") == "GB/s":
             entry["frac_of_runtime_copy"] = round(entry["achieved"] / copy_gbs, 4)
@@ -787,10 +821,15 @@ def main():
         "next_rows": next_rows,
         "cpu_baseline": cpu,
         "reference_rates": {"runtime_copy_GBs": round(copy_gbs, 1),
+                            "vendor_gemm_fwd_TFLOPs": round(vendor["fwd"], 1) if vendor else None,
+                            "vendor_gemm_wgrad_TFLOPs": round(vendor["wgrad"], 1) if vendor else None,
                             "note": "the HIP runtime's device copy of 1 GiB (read + write), HIP events; a GB/s "
                                     "stage's frac_of_runtime_copy is its rate over this (above 1: faster than "
                                     "the runtime's copy). A one-shot 16-byte-per-thread copy kernel measured "
-                                    "about 6.5 TB/s (81% of 8 TB/s), the practical HBM ceiling."},
+                                    "about 6.5 TB/s (81% of 8 TB/s), the practical HBM ceiling. vendor_gemm_*: "
+                                    "hipBLASLt (torch.matmul, bf16) on the same FLOPs as R dense GEMMs, "
+                                    "[P,H]x[H,H'] and [H,P]x[P,H']; a GEMM stage's frac_of_vendor_gemm is its "
+                                    "rate over that."},
         "sweep": sweep,
         "sweep_flatness": flat,
     }
