@@ -3,7 +3,8 @@
 Every buffer is allocated once, with shapes fixed by (R, E, B, S, K, H, Hp):
 nothing depends on the routing, so repeated passes allocate nothing and a
 pass can be captured in a HIP graph.  The forward pass is
-plan -> dispatch -> prefetch -> group GEMM -> combine; the weight backward is
+plan -> prefetch -> dispatch -> group GEMM -> combine (the prefetch needs only
+the plan); the weight backward is
 wgrad -> reduce_grad; with data_grad=True the data backward is
 combine_backward (writes dY and dgates from dout) -> dgrad -> dispatch_backward
 (dX).  Each step is one C-ABI call whose kernels do all the work; this class
