@@ -185,6 +185,7 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(
   int32_t* sdefs = sdef + R;    // [R] exclusive scan of def
   int32_t* sefirst = sdefs + R; // [R]
   int32_t* sncopy = sefirst + R;// [R]
+  int32_t* solist = sT;         // [E] the overflowing experts, ascending (sT is dead by then)
   __shared__ int32_t wsum[kSolveThreads / 64];
   __shared__ int32_t red[3][kSolveThreads / 64];
   const int t = threadIdx.x, nt = blockDim.x, lane = t & 63, w = t >> 6, nw = nt >> 6;
@@ -235,28 +236,38 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(
   block_excl_scan(snpos, E, wsum);
   block_excl_scan(sdefs, R, wsum);
 
-  // contiguous cut: each deficit rank walks the experts its interval overlaps
+  // contiguous cut.  Deficit rank d's interval [lo, hi) of the overflow list overlaps the experts
+  // e in [a, z) with over[e] > 0, where a is the first e with ovstart + over > lo and z the first
+  // e >= a with ovstart >= hi (ovstart is non-decreasing); they are its copies, ascending, and the
+  // j-th of them is the (npos[a] + j)-th overflowing expert overall.
+  for (int e = t; e < E; e += nt)
+    if (sover[e] > 0) solist[snpos[e]] = e;
   for (int d = t; d < R; d += nt) {
     int j = 0, ef = 0;
     if (sdef[d] > 0) {
       const int lo = sdefs[d], hi = lo + sdef[d];
-      int a = 0, b = E;  // first e with ovstart + over > lo
+      int a = 0, b = E;
       while (a < b) {
         const int m = (a + b) >> 1;
         if (sovs[m] + sover[m] > lo) b = m; else a = m + 1;
       }
+      int z = a, y = E;
+      while (z < y) {
+        const int m = (z + y) >> 1;
+        if (sovs[m] >= hi) y = m; else z = m + 1;
+      }
+      const auto npos_at = [&](int e) { return e < E ? snpos[e] : snpos[E - 1] + (sover[E - 1] > 0); };
       ef = a < E ? a : 0;  // a == E only when invalid ids left the deficits larger than the overflow
-      for (int e = a; e < E && sovs[e] < hi; ++e)
-        if (sover[e] > 0) {
-          if (j < B) slot_expert[(int64_t)d * B + j] = e;
-          ++j;
-        }
+      j = npos_at(z) - npos_at(a);
     }
-    for (int jj = min(j, B); jj < B; ++jj) slot_expert[(int64_t)d * B + jj] = -1;
     sefirst[d] = ef;
     sncopy[d] = j;
   }
   __syncthreads();
+  for (int i = t; i < R * B; i += nt) {
+    const int d = i / B, jj = i % B;
+    slot_expert[i] = jj < sncopy[d] ? solist[snpos[sefirst[d]] + jj] : -1;
+  }
 
   // cu_seqlens: one wave per rank, 64 groups at a time
   const int G = E + B;
@@ -276,7 +287,8 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(
           if (f > 0 && snpos[g] - nf >= B) c = f;  // direct read of home row g
         }
       } else if (g < G) {
-        const int e = slot_expert[(int64_t)d * B + (g - E)];
+        const int jj = g - E;  // slot jj < B of rank d, from the LDS tables (not the global output)
+        const int e = jj < sncopy[d] ? solist[snpos[sefirst[d]] + jj] : -1;
         if (e >= 0) c = overlap(sovs[e], sovs[e] + sover[e], d0, d1);
       }
       const int incl = wave_incl_scan(c);
