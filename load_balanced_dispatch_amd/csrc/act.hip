@@ -6,9 +6,9 @@
 // the FFN; read plainly it is the gated expert: a gate|up projection whose rows
 // hold [gate (H') | up (H')], act = silu(gate) * up, then a down projection.
 //
-// Both kernels are HBM streams over the N = R*S*K dispatched rows, one thread per
-// 16-byte chunk of the output row over a one-shot grid (one vector per thread
-// measured fastest for streams on this chip).  Arithmetic is float32 on the
+// Both kernels are HBM streams over the N = R*S*K dispatched rows over one-shot
+// grids: the forward takes two 16-byte output chunks per thread, the backward one;
+// inputs are read with non-temporal loads (each is read once here).  Arithmetic is float32 on the
 // (bf16 or f32) inputs; each result is rounded once to the row dtype.
 #include "moonep_common.h"
 
@@ -29,8 +29,8 @@ struct Vec;
 template <>
 struct Vec<uint16_t> {  // 8 bf16 per 16 bytes
   static constexpr int N = 8;
-  static __device__ __forceinline__ void load(const uint16_t* p, float* f) {
-    const u32x4 q = *reinterpret_cast<const u32x4*>(p);
+  static __device__ __forceinline__ void load(const uint16_t* p, float* f) {  // streamed: non-temporal
+    const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       f[2 * i] = __uint_as_float(q[i] << 16);
@@ -48,7 +48,7 @@ template <>
 struct Vec<float> {  // 4 f32 per 16 bytes
   static constexpr int N = 4;
   static __device__ __forceinline__ void load(const float* p, float* f) {
-    const f32x4 q = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 q = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
 #pragma unroll
     for (int i = 0; i < 4; ++i) f[i] = q[i];
   }
@@ -78,22 +78,38 @@ __device__ __forceinline__ void swiglu_grad1(float g, float u, float da, float& 
   du = da * g * s;
 }
 
-// A[row, c] = silu(Ygu[row, c]) * Ygu[row, Hp + c]; one thread per 16-byte chunk of A.
+// A[row, c] = silu(Ygu[row, c]) * Ygu[row, Hp + c]; each thread takes two 16-byte chunks of A, one in
+// each half of the output, and issues all four loads first (measured 6% faster than one chunk).
 template <typename T>
 __global__ __launch_bounds__(kActThreads) void swiglu_vec(const T* __restrict__ Ygu, T* __restrict__ A,
                                                           int64_t rows, int Hp) {
   constexpr int V = Vec<T>::N;
   const int cpr = Hp / V;
-  const int64_t i = (int64_t)blockIdx.x * kActThreads + threadIdx.x;
-  if (i >= rows * cpr) return;
-  const int64_t row = i / cpr;
-  const int c = (int)(i % cpr) * V;
-  float g[V], u[V], a[V];
-  Vec<T>::load(Ygu + row * 2 * Hp + c, g);
-  Vec<T>::load(Ygu + row * 2 * Hp + Hp + c, u);
+  const int64_t total = rows * cpr, half = (total + 1) / 2;
+  const int64_t i0 = (int64_t)blockIdx.x * kActThreads + threadIdx.x;
+  if (i0 >= half) return;
+  float g[2][V], u[2][V], a[V];
 #pragma unroll
-  for (int j = 0; j < V; ++j) a[j] = swiglu1(g[j], u[j]);
-  Vec<T>::store(A + row * Hp + c, a);
+  for (int h = 0; h < 2; ++h) {
+    const int64_t i = i0 + h * half;
+    if (i < total) {
+      const int64_t row = i / cpr;
+      const int c = (int)(i % cpr) * V;
+      Vec<T>::load(Ygu + row * 2 * Hp + c, g[h]);
+      Vec<T>::load(Ygu + row * 2 * Hp + Hp + c, u[h]);
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int64_t i = i0 + h * half;
+    if (i < total) {
+      const int64_t row = i / cpr;
+      const int c = (int)(i % cpr) * V;
+#pragma unroll
+      for (int j = 0; j < V; ++j) a[j] = swiglu1(g[h][j], u[h][j]);
+      Vec<T>::store(A + row * Hp + c, a);
+    }
+  }
 }
 
 template <typename T>
@@ -150,7 +166,7 @@ int act_launch(const char* name, bool backward, int64_t rows, int Hp, const void
   const T* y = static_cast<const T*>(Ygu);
   T* o = static_cast<T*>(out);
   if (!backward) {
-    if (vec) hipLaunchKernelGGL(swiglu_vec<T>, dim3(grid), dim3(kActThreads), 0, s, y, o, rows, Hp);
+    if (vec) hipLaunchKernelGGL(swiglu_vec<T>, dim3((grid + 1) / 2), dim3(kActThreads), 0, s, y, o, rows, Hp);
     else hipLaunchKernelGGL(swiglu_scalar<T>, dim3(grid), dim3(kActThreads), 0, s, y, o, rows, Hp);
   } else {
     const T* d = static_cast<const T*>(dA);
