@@ -386,12 +386,14 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_grad_kernel(const int32
       for (int u = 0; u < kReduceUnroll; ++u) {
         const int64_t v = c * per_item + u * kReduceThreads + threadIdx.x;
         if (v < nvec) {
-          const f32x4 x = sl[v];
+          // a slot is read once and cleared: non-temporal both ways, so the zeros leave no dirty
+          // lines behind for the next kernels to write back
+          const f32x4 x = __builtin_nontemporal_load(sl + v);
           acc[u][0] = acc[u][0] + x[0];
           acc[u][1] = acc[u][1] + x[1];
           acc[u][2] = acc[u][2] + x[2];
           acc[u][3] = acc[u][3] + x[3];
-          sl[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+          __builtin_nontemporal_store(f32x4{0.f, 0.f, 0.f, 0.f}, sl + v);
         }
       }
     }
