@@ -23,24 +23,6 @@ __device__ __forceinline__ bf16x4 lds_tr4(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
 }
 
-// MFMA 32x32x16 operand whose reduction index k runs along the ROWS of a
-// row-major LDS tile T (leading dimension ld elements): lane l gets
-// T[k0 + 8*(l/32) + i][c0 + l%32], i = 0..7.
-__device__ __forceinline__ bf16x8 operand_rows_k(const uint16_t* T, int ld, int k0, int c0, int lane) {
-  const int grp = lane >> 4, c = lane & 15;
-  const int col = c0 + 16 * (grp & 1) + 4 * (c & 3);
-  const int row = k0 + 8 * (grp >> 1) + (c >> 2);
-  const bf16x4 lo = lds_tr4(T + row * ld + col);
-  const bf16x4 hi = lds_tr4(T + (row + 4) * ld + col);
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-// MFMA 32x32x16 operand whose reduction index k runs along the COLUMNS of a
-// row-major LDS tile T: lane l gets T[r0 + l%32][k0 + 8*(l/32) + i].
-__device__ __forceinline__ bf16x8 operand_cols_k(const uint16_t* T, int ld, int r0, int k0, int lane) {
-  return *reinterpret_cast<const bf16x8*>(T + (r0 + (lane & 31)) * ld + k0 + 8 * (lane >> 5));
-}
-
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
