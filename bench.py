@@ -102,7 +102,6 @@ def load_inputs(L, wl, seed, alpha):
     return idx, gates
 
 
-STAGES = ("plan", "prefetch", "dispatch", "group_gemm", "combine", "wgrad", "reduce_grad")
 
 
 def stage_calls(L, backward):
@@ -299,7 +298,6 @@ STAGE_SOURCE = {"plan": "plan.hip", "dispatch": "move.hip", "prefetch": "move.hi
                 "combine_backward": "move.hip", "dgrad": "ggemm.hip", "dispatch_backward": "move.hip",
                 "swiglu": "act.hip", "swiglu_backward": "act.hip"}
 GEMM_STAGES = ("group_gemm", "wgrad", "dgrad")
-NEXT_STAGES = ("combine_backward", "dgrad", "dispatch_backward")
 CSRC = os.path.join(ROOT, "load_balanced_dispatch_amd", "csrc")
 
 
