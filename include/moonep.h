@@ -108,6 +108,10 @@ size_t moonep_plan_workspace_bytes(moonep_dims d);
  *                                      invalid ids + repeated ids within a token.
  * workspace: moonep_plan_workspace_bytes(d) bytes of device memory, contents
  * ignored on entry.
+ * Limits (MOONEP_EINVAL beyond them): E <= 4096, R <= 4096, and each planner
+ * block keeps per-expert and per-rank tables in LDS, so the largest of
+ * E + max(1024, K), 5E + 4R and 8E + 3R int32 values must fit in 158 KiB
+ * (E = 4096 allows R <= 2048; E = 2048 any R that divides it).
  */
 int moonep_plan(moonep_dims d, const int32_t* topk_idx, int32_t* expert_counts, double* maxvio,
                 int32_t* cu_seqlens, int32_t* slot_expert, int32_t* dest_idx, int32_t* src_of_row,

@@ -21,6 +21,8 @@
 //   plan_emit   grid = U: stable rank of every pair inside its expert (wave
 //               ballot match + per-wave LDS counters, tiles processed in order),
 //               then its destination row.
+#include <algorithm>
+
 #include "block_scan.h"
 #include "moonep_common.h"
 
@@ -34,6 +36,7 @@ constexpr int kSolveThreads = 1024;
 // within 4% of the best on a 1M-pair routing workload
 constexpr int kPairsPerBlock = 1024;
 constexpr int kMaxExperts = 4096;
+constexpr int64_t kPlanMaxDynLds = 160 * 1024 - 2048;  // LDS per block left for the dynamic tables
 constexpr int kMaxRanks = 4096;
 
 struct PlanGeom {
@@ -444,6 +447,14 @@ extern "C" int moonep_plan(moonep_dims d, const int32_t* topk_idx, int32_t* expe
   const int64_t N = n_pairs(d);
   MOONEP_REQUIRE(d.E <= kMaxExperts, "moonep_plan: E=%d exceeds the supported %d", d.E, kMaxExperts);
   MOONEP_REQUIRE(d.R <= kMaxRanks, "moonep_plan: R=%d exceeds the supported %d", d.R, kMaxRanks);
+  const PlanGeom geo = plan_geom(d);
+  // per-block LDS tables of the three kernels, in ints: count E + tpb*K, solve 5E + 4R, emit
+  // (4 + waves)E + 3R; the largest must fit beside the kernels' static arrays
+  const int64_t lds_ints = std::max<int64_t>({(int64_t)d.E + (int64_t)geo.tpb * d.K, 5 * (int64_t)d.E + 4 * (int64_t)d.R,
+                                              (4 + kEmitWaves) * (int64_t)d.E + 3 * (int64_t)d.R});
+  MOONEP_REQUIRE(lds_ints * (int64_t)sizeof(int32_t) <= kPlanMaxDynLds,
+                 "moonep_plan: E=%d with R=%d needs %lld bytes of LDS tables per block, more than %lld", d.E, d.R,
+                 (long long)(lds_ints * (int64_t)sizeof(int32_t)), (long long)kPlanMaxDynLds);
   MOONEP_REQUIRE(expert_counts && maxvio && cu_seqlens && stats && workspace,
                  "moonep_plan: null output or workspace pointer");
   MOONEP_REQUIRE(d.B == 0 || slot_expert, "moonep_plan: slot_expert is null with B > 0");
@@ -451,7 +462,6 @@ extern "C" int moonep_plan(moonep_dims d, const int32_t* topk_idx, int32_t* expe
   MOONEP_REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, "moonep_plan: workspace must be 256-byte aligned");
   hipStream_t s = as_stream(stream);
   clear_stale_error();
-  const PlanGeom geo = plan_geom(d);
   const PlanWs ws = plan_ws(d, workspace);
   const int P = d.S * d.K;
 

@@ -73,6 +73,17 @@ def test_bad_dims_rejected_everywhere(dims, msg):
     assert m.moonep_wgrad_workspace_bytes(d) == 0
 
 
+@pytest.mark.parametrize("R,E,msg", [
+    (4096, 4096, "LDS"),        # emit tables 8E + 3R ints = 176 KiB
+    (4096, 8192, "exceeds"),    # beyond the expert limit
+    (4, 4100, "exceeds"),
+])
+def test_plan_rejects_sizes_beyond_its_lds_tables(R, E, msg):
+    d = m.make_dims(R, E, 8, 1, 2)
+    assert _lib.lib().moonep_plan(d, *([None] * 10)) == _lib.MOONEP_EINVAL
+    assert msg in m.last_error()
+
+
 def test_null_pointers_rejected():
     d = m.make_dims(2, 4, 1, 3, 1)
     L = _lib.lib()

@@ -106,6 +106,11 @@ def test_plan_random_bit_exact(m, seed):
     (1, 5, 2, 1000, 5),      # one rank: nothing can move, K = E
     (8, 64, 8, 2731, 6),     # several count/emit blocks with a ragged last block
     (16, 64, 1, 300, 4),     # many ranks, one slot
+    # largest tables the planner's blocks hold in LDS: emit 8E + 3R ints = 152 KiB
+    (2048, 4096, 2, 2, 2),
+    (512, 4096, 8, 8, 4),    # E at its limit with many blocks of the count/emit grids
+    (2048, 2048, 3, 3, 5),   # 2048 ranks of one expert each
+    (2, 4096, 4, 3, 1500),   # K above the 1024 pairs of a block: one token per block
 ])
 def test_plan_shapes_bit_exact(m, R, E, B, S, K):
     rng = np.random.default_rng(R * 1000 + S)
