@@ -17,6 +17,7 @@ after the step as `next_rows`, and the CPU oracle's rate on a bounded sample.
 
     python bench.py --stats-md run_kernel_stats.csv          (rocprofv3 summary -> markdown)
     python bench.py --traffic-md fetch.csv write.csv         (counter runs -> per-stage HBM bytes)
+    python bench.py --mfma-md counters.csv                   (counter run -> GEMM MFMA utilisation)
 """
 from __future__ import annotations
 
@@ -36,6 +37,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 MFMA_F32_VECTOR_TFLOPS = 157.3  # MI355X fp32 vector
+N_CU, SIMDS_PER_CU, TOP_CLOCK_GHZ = 256, 4, 2.4  # MI355X compute units, SIMDs per CU, peak engine clock
+MFMA_FLOP_PER_INST = 32768  # one v_mfma_f32_32x32x16_bf16, the only MFMA the GEMM kernels issue
+MFMA_COUNTERS = ("SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES")
 
 WORKLOAD_KEYS = {"tiny": "tiny_f32", "mid": "mid_fwd", "large": "large_fwd", "stress": "plan_stress"}
 
@@ -64,6 +68,9 @@ def parse():
                     help="print per-call kernel times of an --ffn-only rocprofv3 kernel_trace.csv; no GPU")
     ap.add_argument("--ffn-traffic-md", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print the per-call HBM traffic of two --ffn-only --profile-pass counter runs; no GPU")
+    ap.add_argument("--mfma-md", metavar="COUNTER_CSV",
+                    help="print the MFMA utilisation of the GEMM kernels from a --profile-pass counter run of "
+                         + " ".join(MFMA_COUNTERS) + "; no GPU")
     ap.add_argument("--profile-pass", action="store_true",
                     help="for counter runs: 1 warm-up + --steps steps of the whole path, then one plain 1 GiB "
                          "device copy whose FETCH_SIZE/WRITE_SIZE calibrate the traffic counters; prints no JSON")
@@ -367,7 +374,7 @@ def load_traffic(wl, target):
             for st, v in rec["stages"].items()}
 
 
-def stage_roofline(name, alg, ms, traffic, f32):
+def stage_roofline(name, alg, ms, traffic, f32, mfma=None):
     gemm = name in GEMM_STAGES
     if gemm:
         bound, unit = ("alu", "TFLOP/s") if f32 else ("mfma", "TFLOP/s")
@@ -387,6 +394,8 @@ def stage_roofline(name, alg, ms, traffic, f32):
         r["least_bytes_per_launch"] = least
     if t:
         r["traffic_over_least_bytes"] = round(t / least, 3)
+    if gemm and not f32:
+        r["mfma_util"] = (mfma or {}).get(name)  # from the committed counter summary, None once stale
     return r
 
 
@@ -442,6 +451,69 @@ def traffic_markdown(fetch_csv, write_csv, wl, target):
                            "write_scale": round(ws, 4)},
            "stages": stages}
     return "\n".join(lines), rec
+
+
+def mfma_markdown(counter_csv, wl, target):
+    """MFMA utilisation of each GEMM kernel from a --profile-pass counter run, averaged over its dispatches.
+
+    SQ_VALU_MFMA_BUSY_CYCLES sums the cycles each SIMD's matrix pipe is busy (32 per 32x32x16 bf16
+    instruction) and SQ_BUSY_CU_CYCLES the cycles each CU has work, so their ratio over 4 SIMDs is the
+    fraction of the kernel's own cycles the matrix pipes compute, and CU-busy cycles per CU over the
+    dispatch's duration give the engine clock it ran at.  The busy cycles over 1024 SIMDs at the 2.4 GHz
+    peak clock for that duration give its fraction of the nominal peak."""
+    per = {}
+    for r in csv.DictReader(open(counter_csv)):
+        base = kernel_base(r["Kernel_Name"])
+        if stage_of(base) not in GEMM_STAGES:
+            continue
+        d = per.setdefault(int(r["Dispatch_Id"]), {"base": base})
+        d["dur_s"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+    kernels = {}
+    for d in per.values():
+        if any(c not in d for c in MFMA_COUNTERS) or d["SQ_INSTS_MFMA"] <= 0:
+            continue  # the tile and schedule kernels beside the GEMMs issue no MFMA
+        kernels.setdefault(d["base"], []).append(d)
+    lines = ["| kernel | stage | dispatches | avg us (counted run) | MFMA instructions | engine clock GHz | "
+             "MFMA busy / CU busy | issued TFLOP/s | of 2.5 PF nominal |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    rec = {"workload": wl.name, "maxvio_target": target, "counters": list(MFMA_COUNTERS), "kernels": {}}
+    for base in sorted(kernels):
+        ds = kernels[base]
+        avg = {k: sum(d[k] for d in ds) / len(ds) for k in MFMA_COUNTERS + ("dur_s",)}
+        busy = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (SIMDS_PER_CU * avg["SQ_BUSY_CU_CYCLES"])
+        clock = avg["SQ_BUSY_CU_CYCLES"] / N_CU / avg["dur_s"] / 1e9
+        issued = avg["SQ_INSTS_MFMA"] * MFMA_FLOP_PER_INST / avg["dur_s"] / 1e12
+        nominal = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (N_CU * SIMDS_PER_CU * TOP_CLOCK_GHZ * 1e9 * avg["dur_s"])
+        st = stage_of(base)
+        rec["kernels"][base] = {"stage": st, "dispatches": len(ds), "avg_us": round(avg["dur_s"] * 1e6, 2),
+                                "mfma_insts": round(avg["SQ_INSTS_MFMA"]),
+                                "engine_clock_ghz": round(clock, 3), "mfma_busy_of_cu_busy": round(busy, 4),
+                                "issued_tflops": round(issued, 1), "of_nominal_peak": round(nominal, 4),
+                                "sources": sources_digest(st)}
+        lines.append(f"| `{base}` | {st} | {len(ds)} | {avg['dur_s'] * 1e6:.1f} | {avg['SQ_INSTS_MFMA']:.4g} | "
+                     f"{clock:.2f} | {busy:.3f} | {issued:.0f} | {nominal:.3f} |")
+    return "\n".join(lines), rec
+
+
+def load_mfma(wl, target):
+    """Per GEMM stage, the MFMA utilisation of profiles/mfma_util_<workload>.md, or None for a stage whose
+    kernel source has changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"mfma_util_{wl.name}.md")
+    if not os.path.exists(path):
+        return {}
+    m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
+    if not m:
+        return {}
+    rec = json.loads(m.group(1))
+    if rec.get("workload") != wl.name or rec.get("maxvio_target") != target:
+        return {}
+    out = {}
+    for k in rec["kernels"].values():
+        ok = k["sources"] == sources_digest(k["stage"])
+        out[k["stage"]] = ({"mfma_busy_of_cu_busy": k["mfma_busy_of_cu_busy"],
+                            "engine_clock_ghz": k["engine_clock_ghz"]} if ok else None)
+    return out
 
 
 def label_ffn_dispatches(names):
@@ -668,6 +740,14 @@ def main():
     if args.ffn_stats_md:
         print(ffn_stats_markdown(args.ffn_stats_md))
         return
+    if args.mfma_md:
+        table, rec = mfma_markdown(args.mfma_md, wl, head_target)
+        print(table)
+        print()
+        print("```json")
+        print(json.dumps(rec, indent=1))
+        print("```")
+        return
     if args.ffn_traffic_md or args.traffic_md:
         if args.ffn_traffic_md:
             table, rec = ffn_traffic_markdown(args.ffn_traffic_md[0], args.ffn_traffic_md[1], wl)
@@ -750,13 +830,14 @@ def main():
             comp["reduce_grad_GBs"] = (alg["reduce_grad"] / (st["reduce_grad"] * 1e-3) / 1e9
                                        if alg["reduce_grad"] else None)
     traffic = load_traffic(wl, head_target)
-    rooflines = {n: stage_roofline(n, alg, st[n], traffic, wl.dtype == "f32") for n in st}
+    mfma = load_mfma(wl, head_target)
+    rooflines = {n: stage_roofline(n, alg, st[n], traffic, wl.dtype == "f32", mfma) for n in st}
     next_rows = None
     if backward:
         load_inputs(L, wl, args.seed, h["alpha"])  # the headline routing again (the sweep moved it)
         nx = time_next_rows(L, args.steps, args.warmup)
         log(f"backward of the data path: {nx}")
-        next_rows = {n: stage_roofline(n, alg, nx[n], traffic, wl.dtype == "f32") for n in nx}
+        next_rows = {n: stage_roofline(n, alg, nx[n], traffic, wl.dtype == "f32", mfma) for n in nx}
         if wl.dtype == "bf16" and not args.no_ffn:
             log("full gated expert FFN (forward + backward)")
             next_rows["ffn"] = time_ffn(wl, args.seed, h["alpha"], max(3, args.steps // 4), 2)

@@ -160,3 +160,34 @@ def test_hot_rank_factor_extremes():
     # each rank's pairs spread evenly over all ranks' experts: every rank holds exactly P
     flat = (np.arange(wl.R * wl.S * wl.K) % wl.E).reshape(wl.R, wl.S, wl.K)
     assert bench.hot_rank_factor(flat, wl) == 1.0
+
+
+def test_mfma_table_from_counters(tmp_path):
+    # two forward GEMM dispatches of 1 ms whose CUs are busy 1.9e6 cycles each at half the matrix pipes'
+    # cycles, one wgrad dispatch, and the tile kernel beside them, which issues no MFMA
+    path = str(tmp_path / "sq.csv")
+    fields = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    rows = []
+    for disp, key, dur_ns, insts in ((1, "fwd", 1_000_000, 1e7), (2, "tiles", 4_000, 0.0), (3, "fwd", 1_000_000, 1e7),
+                                     (4, "wgrad", 2_000_000, 2e7)):
+        cu = 256 * 1.9e9 * dur_ns * 1e-9
+        vals = {"SQ_INSTS_MFMA": insts, "SQ_BUSY_CU_CYCLES": cu, "SQ_VALU_MFMA_BUSY_CYCLES": 0.5 * 4 * cu if insts else 0}
+        for c, v in vals.items():
+            rows.append({"Dispatch_Id": disp, "Kernel_Name": NAMES[key], "Counter_Name": c, "Counter_Value": v,
+                         "Start_Timestamp": 10_000 * disp, "End_Timestamp": 10_000 * disp + dur_ns})
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=fields)
+        w.writeheader()
+        w.writerows(rows)
+    from synthetic import WORKLOADS
+    table, rec = bench.mfma_markdown(path, WORKLOADS["mid_fwd"], 1.0)
+    k = rec["kernels"]
+    assert set(k) == {"ggemm_bf16<false>", "wgrad_bf16"}
+    f = k["ggemm_bf16<false>"]
+    assert f["stage"] == "group_gemm" and f["dispatches"] == 2
+    assert f["engine_clock_ghz"] == 1.9 and f["mfma_busy_of_cu_busy"] == 0.5
+    assert f["issued_tflops"] == round(1e7 * 32768 / 1e-3 / 1e12, 1)
+    # half the pipes' cycles at 1.9 GHz of a 2.4 GHz peak
+    assert f["of_nominal_peak"] == round(0.5 * 1.9 / 2.4, 4)
+    assert k["wgrad_bf16"]["stage"] == "wgrad" and k["wgrad_bf16"]["avg_us"] == 2000.0
+    assert "`ggemm_bf16<false>` | group_gemm | 2 |" in table
