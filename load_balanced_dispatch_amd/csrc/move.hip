@@ -6,11 +6,12 @@
 // layout"):
 //   dispatch    one wave per 64-element piece of a token's row: read once into
 //               registers, stored K times (fused permute into the expert-grouped buffer).
-//   prefetch    persistent blocks copy every used slot's [H,Hp] expert matrix.
+//   prefetch    persistent blocks copy every used slot's [H,Hp] expert matrix, one item ahead.
 //   combine     one thread per 16 bytes of input row: K gathers issued together
 //               (non-temporal: Yp is read once), fp32 FMA in k order.
 //   reduce_grad persistent blocks fold each expert's slot gradients (ranks in
-//               ascending order) into the home gradient and zero the slots.
+//               ascending order, a batch of slots loaded at once) into the home
+//               gradient and zero the slots.
 #include "block_scan.h"
 #include "moonep_common.h"
 
@@ -56,6 +57,13 @@ constexpr int kCopyUnroll = 4;
 constexpr int kCopyBlocksPerCU = 8;  // measured: 8 beat 16 by 5% on the large workload (equal on mid); 4 and 64 slower
 constexpr int kMaxSlots = 32768;
 
+// Persistent copy of every used slot, in items of kCopyThreads * kCopyUnroll vectors.  The loads of
+// a block's next item are issued before the stores of its current one: on gfx950 one counter
+// (vmcnt) tracks loads and stores in issue order, so a wait for loads issued after a store also
+// waits for that store to complete; loading one item ahead keeps the stores off that wait.  In the
+// whole step this took the large workload's prefetch from 101 / 109 / 121 / 153 us to
+// 98 / 108 / 120 / 147 us at maxvio 0.5 / 1 / 2 / 4 and the mid one's from 22.1 to 17.8 us at
+// maxvio 0.  Non-temporal slot stores were no faster in the step, and non-temporal loads slower.
 template <typename V>
 __global__ __launch_bounds__(kCopyThreads) void prefetch_slots(const V* __restrict__ W_home,
                                                                const int32_t* __restrict__ slot_expert,
@@ -72,23 +80,35 @@ __global__ __launch_bounds__(kCopyThreads) void prefetch_slots(const V* __restri
   const int64_t per_item = (int64_t)kCopyThreads * kCopyUnroll;
   const int64_t chunks = (nvec + per_item - 1) / per_item;
   const int64_t items = (int64_t)n * chunks;
-  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+  auto load = [&](int64_t it, V* r) {
     const int s = used[it / chunks];
-    const int64_t c = it % chunks;
-    const int e = slot_expert[s];
-    const V* src = W_home + (int64_t)e * nvec;
-    V* dst = W_slots + (int64_t)s * nvec;
-    V r[kCopyUnroll];
+    const V* src = W_home + (int64_t)slot_expert[s] * nvec;
+    const int64_t v0 = (it % chunks) * per_item + threadIdx.x;
 #pragma unroll
-    for (int u = 0; u < kCopyUnroll; ++u) {
-      const int64_t v = c * per_item + u * kCopyThreads + threadIdx.x;
-      if (v < nvec) r[u] = src[v];
-    }
+    for (int u = 0; u < kCopyUnroll; ++u)
+      if (v0 + u * kCopyThreads < nvec) r[u] = src[v0 + u * kCopyThreads];
+  };
+  auto store = [&](int64_t it, const V* r) {
+    V* dst = W_slots + (int64_t)used[it / chunks] * nvec;
+    const int64_t v0 = (it % chunks) * per_item + threadIdx.x;
 #pragma unroll
-    for (int u = 0; u < kCopyUnroll; ++u) {
-      const int64_t v = c * per_item + u * kCopyThreads + threadIdx.x;
-      if (v < nvec) dst[v] = r[u];
-    }
+    for (int u = 0; u < kCopyUnroll; ++u)
+      if (v0 + u * kCopyThreads < nvec) dst[v0 + u * kCopyThreads] = r[u];
+  };
+  // two register buffers, alternating, so that the indices into them stay compile-time constants
+  V a[kCopyUnroll], b[kCopyUnroll];
+  int64_t it = blockIdx.x;
+  if (it < items) load(it, a);
+  while (it < items) {
+    int64_t nx = it + gridDim.x;
+    if (nx < items) load(nx, b);
+    store(it, a);
+    it = nx;
+    if (it >= items) break;
+    nx = it + gridDim.x;
+    if (nx < items) load(nx, a);
+    store(it, b);
+    it = nx;
   }
 }
 
@@ -322,9 +342,21 @@ __global__ __launch_bounds__(256) void combine_bwd_scalar(const float* __restric
 // ------------------------------------------------------------------ reduce_grad
 
 constexpr int kReduceThreads = 256;
-constexpr int kReduceUnroll = 4;
-constexpr int kReduceBlocksPerCU = 16;  // measured: 4 and 64 per CU are both slower
+// Measured in the whole step (bitwise-identical results): 2 vectors per thread, slots in batches
+// of 4 and 4 blocks per CU took the mid workload's reduce_grad from 54.6 / 51.4 / 73.9 us to
+// 48.9 / 46.6 / 63.3 us at maxvio 0 / 2 / 3 (equal at maxvio 1 and within 3% on the large one)
+// against 4 vectors, one slot at a time and 16 blocks per CU.
+constexpr int kReduceUnroll = 2;
+constexpr int kReduceBatch = 4;
+constexpr int kReduceBlocksPerCU = 4;
 constexpr size_t kMaxDynLds = 160 * 1024 - 1024;
+
+__device__ __forceinline__ void add4(f32x4& a, const f32x4& x) {
+  a[0] = a[0] + x[0];
+  a[1] = a[1] + x[1];
+  a[2] = a[2] + x[2];
+  a[3] = a[3] + x[3];
+}
 
 __global__ __launch_bounds__(kReduceThreads) void reduce_grad_kernel(const int32_t* __restrict__ slot_expert,
                                                                      f32x4* __restrict__ dW_home,
@@ -366,42 +398,53 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_grad_kernel(const int32
       if (sslot[s] == e) lslot[p++] = s;
   }
   __syncthreads();
-  const int64_t per_item = (int64_t)kReduceThreads * kReduceUnroll;
+  constexpr int U = kReduceUnroll, CB = kReduceBatch, T = kReduceThreads;
+  const int64_t per_item = (int64_t)T * U;
   const int64_t chunks = (nvec + per_item - 1) / per_item;
   const int64_t items = (int64_t)n * chunks;
   for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
     const int i = (int)(it / chunks);
-    const int64_t c = it % chunks;
-    const int e = elist[i];
-    f32x4 acc[kReduceUnroll];
-    f32x4* home = dW_home + (int64_t)e * nvec;
+    const int64_t v0 = (it % chunks) * per_item + threadIdx.x;
+    f32x4* home = dW_home + (int64_t)elist[i] * nvec;
+    f32x4 acc[U];
 #pragma unroll
-    for (int u = 0; u < kReduceUnroll; ++u) {
-      const int64_t v = c * per_item + u * kReduceThreads + threadIdx.x;
-      if (v < nvec) acc[u] = home[v];
-    }
-    for (int p = loff[i]; p < loff[i + 1]; ++p) {
-      f32x4* sl = dW_slots + (int64_t)lslot[p] * nvec;
+    for (int u = 0; u < U; ++u)
+      if (v0 + u * T < nvec) acc[u] = home[v0 + u * T];
+    // slots in batches of CB: every load of a batch is issued before its adds (which stay in rank
+    // order) and before its stores, so the batch's loads wait on one memory latency together
+    const int pa = loff[i], pe = loff[i + 1];
+    for (int p0 = pa; p0 < pe; p0 += CB) {
+      f32x4 x[CB][U];
+      f32x4* sl[CB];
 #pragma unroll
-      for (int u = 0; u < kReduceUnroll; ++u) {
-        const int64_t v = c * per_item + u * kReduceThreads + threadIdx.x;
-        if (v < nvec) {
-          // a slot is read once and cleared: non-temporal both ways, so the zeros leave no dirty
-          // lines behind for the next kernels to write back
-          const f32x4 x = __builtin_nontemporal_load(sl + v);
-          acc[u][0] = acc[u][0] + x[0];
-          acc[u][1] = acc[u][1] + x[1];
-          acc[u][2] = acc[u][2] + x[2];
-          acc[u][3] = acc[u][3] + x[3];
-          __builtin_nontemporal_store(f32x4{0.f, 0.f, 0.f, 0.f}, sl + v);
+      for (int q = 0; q < CB; ++q) {
+        sl[q] = dW_slots + (int64_t)lslot[min(p0 + q, pe - 1)] * nvec;
+        if (p0 + q < pe) {
+#pragma unroll
+          for (int u = 0; u < U; ++u)
+            if (v0 + u * T < nvec)
+              x[q][u] = __builtin_nontemporal_load(sl[q] + v0 + u * T);
         }
       }
+#pragma unroll
+      for (int q = 0; q < CB; ++q)
+        if (p0 + q < pe) {
+#pragma unroll
+          for (int u = 0; u < U; ++u) add4(acc[u], x[q][u]);
+        }
+      // a slot is read once and cleared: the zeros are stored non-temporally, so they leave no
+      // dirty lines behind for the next kernels to write back
+#pragma unroll
+      for (int q = 0; q < CB; ++q)
+        if (p0 + q < pe) {
+#pragma unroll
+          for (int u = 0; u < U; ++u)
+            if (v0 + u * T < nvec) __builtin_nontemporal_store(f32x4{0.f, 0.f, 0.f, 0.f}, sl[q] + v0 + u * T);
+        }
     }
 #pragma unroll
-    for (int u = 0; u < kReduceUnroll; ++u) {
-      const int64_t v = c * per_item + u * kReduceThreads + threadIdx.x;
-      if (v < nvec) home[v] = acc[u];
-    }
+    for (int u = 0; u < U; ++u)
+      if (v0 + u * T < nvec) home[v0 + u * T] = acc[u];
   }
 }
 
