@@ -855,10 +855,15 @@ def main():
     for tgt in points:
         r = results[tgt]
         fwd = sum(r["stages"].get(n, 0.0) for n in ("plan", "dispatch", "prefetch", "group_gemm", "combine"))
+        # each stage's roofline fraction at this point (prefetch and reduce_grad bytes follow its copies)
+        alg_p = algorithmic(wl, r["stats"], r["slots"], L)
+        frac_p = {n: stage_roofline(n, alg_p, ms_n, {}, wl.dtype == "f32")["frac"]
+                  for n, ms_n in r["stages"].items() if alg_p.get(n)}
         sweep.append({"maxvio_target": tgt, "maxvio": round(r["maxvio"], 4), "ms_per_step": round(r["ms"], 4),
                       "forward_ms": round(fwd, 4), "copies_slotted_direct": r["stats"][:3],
                       "hot_rank_factor": round(r["hot_rank"], 4),
-                      "stages_ms": {k: round(v, 4) for k, v in r["stages"].items()}})
+                      "stages_ms": {k: round(v, 4) for k, v in r["stages"].items()},
+                      "roofline_frac": frac_p})
     sweep.sort(key=lambda x: (x["maxvio_target"] is None, x["maxvio_target"]))
     flat = None
     if len(sweep) > 1:  # every point against the lowest-maxvio point: within +-10% is flat
