@@ -334,6 +334,29 @@ def test_reduce_grad_rank_order_bitwise(m, R, E, B, H, Hp):
     assert_sum_close(hs.cpu().numpy(), ref_h64, scale_h, 1e-5, "reduce_grad vs float64")
 
 
+@pytest.mark.parametrize("H,Hp", [(24, 40), (64, 44)])
+def test_reduce_grad_many_copies_of_one_expert(m, H, Hp):
+    # expert 0 is in every token's top-2, so its home rank overflows into all 15 other ranks: 15 copies,
+    # several batches of slot loads per item; H*Hp/4 = 240 or 704 vectors leaves a partial item
+    R, E, B, S, K = 16, 16, 2, 40, 2
+    rng = np.random.default_rng(7)
+    topk = np.zeros((R, S, K), dtype=np.int32)
+    topk[:, :, 1] = rng.integers(1, E, size=(R, S))
+    p = oplanner.plan(topk, E, B)
+    se = p.slot_expert.reshape(-1)
+    assert int((se == 0).sum()) == R - 1
+    hs = rand_tensor((E, H, Hp), torch.float32, seed=41)
+    ss = rand_tensor((R, B, H, Hp), torch.float32, seed=42) * 1e3
+    ref_h32 = hs.cpu().numpy().copy()
+    ref_s32 = ss.cpu().numpy().copy()
+    olayer.reduce_grad(p.slot_expert, ref_h32, ref_s32, dtype=np.float32)
+    say("reduce_grad many copies", R, E, B, H, Hp)
+    m.moonep_reduce_grad(m.make_dims(R, E, B, S, K), H, Hp, i32(p.slot_expert), hs, ss)
+    torch.cuda.synchronize()
+    assert np.array_equal(hs.cpu().numpy(), ref_h32)  # float32, ranks ascending, bit for bit
+    assert np.array_equal(ss.cpu().numpy(), ref_s32)  # consumed slots zero, unused slots untouched
+
+
 # ------------------------------------------------------------------ tiny workload end to end
 
 
