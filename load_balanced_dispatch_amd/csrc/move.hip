@@ -345,7 +345,9 @@ constexpr int kReduceThreads = 256;
 // Measured in the whole step (bitwise-identical results): 2 vectors per thread, slots in batches
 // of 4 and 4 blocks per CU took the mid workload's reduce_grad from 54.6 / 51.4 / 73.9 us to
 // 48.9 / 46.6 / 63.3 us at maxvio 0 / 2 / 3 (equal at maxvio 1 and within 3% on the large one)
-// against 4 vectors, one slot at a time and 16 blocks per CU.
+// against 4 vectors, one slot at a time and 16 blocks per CU.  Each block first lists every
+// expert's slots: counting them with LDS atomics and placing them with one wave's ballots (instead
+// of a loop over all slots per expert) cut that setup from about 6.5 to 0.7 us.
 constexpr int kReduceUnroll = 2;
 constexpr int kReduceBatch = 4;
 constexpr int kReduceBlocksPerCU = 4;
@@ -364,38 +366,48 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_grad_kernel(const int32
                                                                      int E, int64_t nvec) {
   extern __shared__ int32_t sh[];
   const int RB = R * B;
-  int32_t* sslot = sh;            // [RB] expert held by each slot, -1 unused
-  int32_t* flag = sslot + RB;     // [E]  expert has at least one copy
-  int32_t* elist = flag + E;      // [E]  experts with copies, ascending
-  int32_t* loff = elist + E;      // [E+1] CSR offsets into lslot
-  int32_t* lslot = loff + E + 1;  // [RB] slots of each listed expert, ranks ascending
+  int32_t* sslot = sh;          // [RB] expert held by each slot, -1 unused
+  int32_t* cnt = sslot + RB;    // [E]  copies of each expert
+  int32_t* eoff = cnt + E;      // [E]  start of expert e's slots in lslot
+  int32_t* elist = eoff + E;    // [E]  experts with copies, ascending
+  int32_t* lslot = elist + E;   // [RB] the slots of each listed expert, ranks ascending
   __shared__ int32_t wsum[kReduceThreads / 64];
-  for (int e = threadIdx.x; e < E; e += blockDim.x) flag[e] = 0;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
   __syncthreads();
   for (int s = threadIdx.x; s < RB; s += blockDim.x) {
     const int e = slot_expert[s];
     const bool ok = e >= 0 && e < E;
     sslot[s] = ok ? e : -1;
-    if (ok) flag[e] = 1;  // every writer stores the same value
+    if (ok) atomicAdd(&cnt[e], 1);
   }
   __syncthreads();
-  const int n = block_compact(E, [&](int e) { return flag[e] != 0; }, elist, wsum);
-  // slots of each listed expert in ascending (rank, j) order; a rank holds an expert at most once
-  for (int i = threadIdx.x; i < n; i += blockDim.x) {
-    const int e = elist[i];
-    int c = 0;
-    for (int s = 0; s < RB; ++s) c += sslot[s] == e;
-    loff[i] = c;
-  }
+  const int n = block_compact(E, [&](int e) { return cnt[e] > 0; }, elist, wsum);
+  for (int e = threadIdx.x; e < E; e += blockDim.x) eoff[e] = cnt[e];
   __syncthreads();
-  const int total = block_excl_scan(loff, n, wsum);
-  if (threadIdx.x == 0) loff[n] = total;
-  __syncthreads();
-  for (int i = threadIdx.x; i < n; i += blockDim.x) {
-    const int e = elist[i];
-    int p = loff[i];
-    for (int s = 0; s < RB; ++s)
-      if (sslot[s] == e) lslot[p++] = s;
+  block_excl_scan(eoff, E, wsum);
+  // each used slot's place in its expert's list, slots in ascending order: wave 0 takes the slots
+  // 64 at a time; a lane's rank among the lanes holding the same expert comes from ballots, the
+  // slots of earlier rounds from cnt, reused as a running count that ends at the total again
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    for (int e = lane; e < E; e += 64) cnt[e] = 0;
+    for (int s0 = 0; s0 < RB; s0 += 64) {
+      const int sl = s0 + lane;
+      const int e = sl < RB ? sslot[sl] : -1;
+      int before = 0, group = 0;
+      uint64_t todo = __ballot(e >= 0);
+      while (todo) {
+        const int el = __shfl(e, __builtin_ctzll(todo), 64);
+        const uint64_t m = __ballot(e == el);
+        if (e == el) {
+          before = __popcll(m & lanemask_lt());
+          group = __popcll(m);
+        }
+        todo &= ~m;
+      }
+      if (e >= 0) lslot[eoff[e] + cnt[e] + before] = sl;
+      if (e >= 0 && before == 0) cnt[e] += group;  // read above by every lane of the group first
+    }
   }
   __syncthreads();
   constexpr int U = kReduceUnroll, CB = kReduceBatch, T = kReduceThreads;
@@ -403,16 +415,16 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_grad_kernel(const int32
   const int64_t chunks = (nvec + per_item - 1) / per_item;
   const int64_t items = (int64_t)n * chunks;
   for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
-    const int i = (int)(it / chunks);
+    const int e = elist[(int)(it / chunks)];
     const int64_t v0 = (it % chunks) * per_item + threadIdx.x;
-    f32x4* home = dW_home + (int64_t)elist[i] * nvec;
+    f32x4* home = dW_home + (int64_t)e * nvec;
     f32x4 acc[U];
 #pragma unroll
     for (int u = 0; u < U; ++u)
       if (v0 + u * T < nvec) acc[u] = home[v0 + u * T];
     // slots in batches of CB: every load of a batch is issued before its adds (which stay in rank
     // order) and before its stores, so the batch's loads wait on one memory latency together
-    const int pa = loff[i], pe = loff[i + 1];
+    const int pa = eoff[e], pe = pa + cnt[e];
     for (int p0 = pa; p0 < pe; p0 += CB) {
       f32x4 x[CB][U];
       f32x4* sl[CB];
@@ -631,7 +643,7 @@ extern "C" int moonep_reduce_grad(moonep_dims d, int32_t H, int32_t Hp, const in
   hipStream_t s = as_stream(stream);
   clear_stale_error();
   const int64_t nel = (int64_t)H * Hp;
-  const size_t lds = ((size_t)2 * d.R * d.B + 3 * (size_t)d.E + 1) * sizeof(int32_t);
+  const size_t lds = ((size_t)2 * d.R * d.B + 3 * (size_t)d.E) * sizeof(int32_t);
   if (nel % 4 == 0 && lds <= kMaxDynLds && aligned16(dW_home) && aligned16(dW_slots)) {
     if (lds > 65536)
       (void)hipFuncSetAttribute((const void*)reduce_grad_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
