@@ -194,6 +194,29 @@ def test_prefetch_bit_exact_and_unused_slots_untouched(m, dtype, H, Hp):
     assert np.array_equal(Ws.cpu().float().numpy(), ref)
 
 
+def test_prefetch_several_items_per_block(m):
+    # expert 0 is in every token's top-2, so all 7 other ranks take a copy of it: 7 slots of
+    # 2047 x 4080 bf16 (1020 items of 1024 vectors each, the last one partial) are 3-4 items for each
+    # of the persistent blocks, which load one item ahead of their stores
+    R, E, B, S, K, H, Hp = 8, 8, 2, 32, 2, 2047, 4080
+    rng = np.random.default_rng(11)
+    topk = np.zeros((R, S, K), dtype=np.int32)
+    topk[:, :, 1] = rng.integers(1, E, size=(R, S))
+    p = oplanner.plan(topk, E, B)
+    used = [(r, j, int(p.slot_expert[r, j])) for r in range(R) for j in range(B) if p.slot_expert[r, j] >= 0]
+    assert sum(e == 0 for _, _, e in used) == R - 1
+    W = rand_tensor((E, H, Hp), torch.bfloat16, seed=13)
+    Ws = torch.full((R, B, H, Hp), 7.0, dtype=torch.bfloat16, device=DEV)
+    say("prefetch several items per block", R, E, B, H, Hp)
+    m.moonep_prefetch(m.make_dims(R, E, B, S, K), H, Hp, W, i32(p.slot_expert), Ws)
+    torch.cuda.synchronize()
+    for r in range(R):  # W_slots[r, j] == W_home[slot_expert[r, j]] bit for bit; unused slots untouched
+        for j in range(B):
+            e = int(p.slot_expert[r, j])
+            want = W[e] if e >= 0 else torch.full((H, Hp), 7.0, dtype=torch.bfloat16, device=DEV)
+            assert torch.equal(Ws[r, j].view(torch.int16), want.view(torch.int16)), (r, j, e)
+
+
 # ------------------------------------------------------------------ group GEMM
 
 
