@@ -331,7 +331,10 @@ def test_wgrad_accumulates(m, dtype, R, E, B, S, K, H, Hp):
                     assert np.array_equal(np64(dWs[r, j]), init_s[r, j])
 
 
-@pytest.mark.parametrize("R,E,B,H,Hp", [(8, 64, 8, 64, 44), (4, 16, 4, 3, 5), (8, 32, 4, 128, 256)])
+# the last three have R*B = 128 or 200 slots: the per-block slot lists are built 64 slots per round,
+# with copies of one expert in several rounds
+@pytest.mark.parametrize("R,E,B,H,Hp", [(8, 64, 8, 64, 44), (4, 16, 4, 3, 5), (8, 32, 4, 128, 256),
+                                        (16, 64, 8, 16, 24), (20, 40, 10, 32, 20), (32, 64, 4, 16, 16)])
 def test_reduce_grad_rank_order_bitwise(m, R, E, B, H, Hp):
     rng = np.random.default_rng(E)
     S, K = 80, 4
