@@ -191,3 +191,36 @@ def test_mfma_table_from_counters(tmp_path):
     assert f["of_nominal_peak"] == round(0.5 * 1.9 / 2.4, 4)
     assert k["wgrad_bf16"]["stage"] == "wgrad" and k["wgrad_bf16"]["avg_us"] == 2000.0
     assert "`ggemm_bf16<false>` | group_gemm | 2 |" in table
+
+
+def test_stage_roofline_fraction_and_algorithmic_bytes():
+    # the per-point roofline fractions of the sweep: achieved = algorithmic work / time, frac = achieved / peak;
+    # prefetch moves 2*H*H'*b per slotted copy, reduce_grad 4*H*H'*(2 per expert with copies + 2 per copy)
+    import numpy as np
+    from synthetic import WORKLOADS
+
+    wl = WORKLOADS["mid_fwd"]
+
+    class FakeLayer:  # algorithmic() reads only the plan's cu_seqlens from the layer
+        def __init__(self):
+            import torch
+            G = wl.E + wl.B
+            cu = np.zeros((wl.R, G + 1), dtype=np.int32)
+            cu[:, 1:] = np.linspace(0, wl.P, G + 1, dtype=np.int64)[1:].astype(np.int32)
+            self.cu_seqlens = torch.as_tensor(cu)
+
+    slots = -np.ones((wl.R, wl.B), dtype=np.int32)
+    slots[1, 0] = slots[2, 0] = slots[3, 1] = 5  # three copies of expert 5
+    slots[4, 0] = 9                              # one copy of expert 9
+    stats = [4, 4, 0, 0]
+    alg = bench.algorithmic(wl, stats, slots, FakeLayer())
+    hh = wl.H * wl.Hp
+    assert alg["prefetch"] == 2 * hh * 2 * 4
+    assert alg["reduce_grad"] == 4 * hh * (2 * 2 + 2 * 4)
+    assert alg["group_gemm"] == 2 * wl.N * hh
+    r = bench.stage_roofline("reduce_grad", alg, 0.05, {}, False)
+    assert r["unit"] == "GB/s" and r["bound"] == "hbm"
+    assert abs(r["achieved"] - alg["reduce_grad"] / 0.05e-3 / 1e9) < 0.01
+    assert abs(r["frac"] - r["achieved"] / bench.HBM_PEAK_GBS) < 1e-4
+    g = bench.stage_roofline("group_gemm", alg, 1.0, {}, False)
+    assert g["unit"] == "TFLOP/s" and abs(g["frac"] - (alg["group_gemm"] / 1e-3 / 1e12) / bench.MFMA_BF16_PEAK_TFLOPS) < 1e-4
