@@ -424,6 +424,15 @@ int group_gemm_launch(const char* name, moonep_dims d, int32_t H, int32_t Hp, mo
   MOONEP_REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, "%s: workspace must be 256-byte aligned",
                  name);
   MOONEP_REQUIRE(n_groups(d) < (int64_t(1) << 30), "%s: too many groups", name);
+  {
+    // rows of 16-byte multiples move as 16-byte vectors: their base pointers must be 16-byte aligned
+    const int64_t eb = (int64_t)elem_bytes(t);
+    const int64_t a_row = (BT ? Hp : H) * eb, c_row = (BT ? H : Hp) * eb, w_row = (int64_t)Hp * eb;
+    MOONEP_REQUIRE(a_row % 16 || aligned16(A), "%s: the input rows must be 16-byte aligned", name);
+    MOONEP_REQUIRE(c_row % 16 || aligned16(C), "%s: the output rows must be 16-byte aligned", name);
+    MOONEP_REQUIRE(w_row % 16 || (aligned16(W_home) && (d.B == 0 || aligned16(W_slots))),
+                   "%s: the weight rows must be 16-byte aligned", name);
+  }
   hipStream_t s = as_stream(stream);
   clear_stale_error();
   int32_t* t256 = static_cast<int32_t*>(workspace);

@@ -155,3 +155,16 @@ def test_build_script_loads_without_the_library():
     spec.loader.exec_module(mod)
     assert callable(mod.build) and mod.ARCH == "gfx950"
     assert "-packed-fp32-ops" in mod.FLAGS
+
+
+@pytest.mark.parametrize("entry", ["moonep_group_gemm", "moonep_group_gemm_dgrad"])
+@pytest.mark.parametrize("which,msg", [(0, "input rows"), (5, "output rows"), (1, "weight rows"), (2, "weight rows")])
+def test_gemm_rejects_misaligned_rows(entry, which, msg):
+    # 16-byte rows move as 16-byte vectors, so an offset view (here 2 bytes) is refused before any launch;
+    # the pointers are never dereferenced
+    d = m.make_dims(2, 4, 1, 3, 1)
+    ptrs = [0x10000, 0x20000, 0x30000, 0x40000, 0x50000, 0x60000]  # A, W_home, W_slots, cu_seqlens, C, ws
+    ptrs[{0: 0, 1: 1, 2: 2, 5: 4}[which]] += 2
+    rc = getattr(_lib.lib(), entry)(d, 64, 64, _lib.MOONEP_BF16, *ptrs, None)
+    assert rc == _lib.MOONEP_EINVAL
+    assert msg in m.last_error()
