@@ -1,19 +1,23 @@
 """Benchmark of the balanced expert-parallel MoE layer on one MI355X.
 
 A step is one pass of the whole hot path over one batch of synthetic input:
-plan -> dispatch -> prefetch -> group GEMM -> combine -> wgrad -> reduce_grad,
+plan -> prefetch -> dispatch -> group GEMM -> combine -> wgrad -> reduce_grad,
 with every input already resident in HBM.  Prints ONE JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--workload mid|large|stress|tiny]
-                    [--maxvio T] [--no-sweep] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload large|mid|stress|tiny]
+                    [--maxvio T] [--no-sweep] [--no-extras] [--no-ffn] [--no-cpu-baseline]
 
-Default workload: R8 E64 K6 S4096 H2048 H'1408 B8 (bf16 activations and
-weights, fp32 gradients), routing skew calibrated to maxvio ~ 1; the sweep adds
-maxvio ~ 0, 2, 3.  value = token-expert pairs per second through the whole
-step; the JSON also carries plan+dispatch pairs/s, group-GEMM TFLOP/s and
-reduce_grad GB/s, every stage's roofline (the longest stage's as `roofline`),
-the backward of the data path (combine backward, dgrad, dispatch backward) timed
-after the step as `next_rows`, and the CPU oracle's rate on a bounded sample.
+Default workload: R8 E256 K8 S4096 H7168 H'2048 B32 (bf16 activations and
+weights, fp32 gradients; the [288, 7168, 2048] weight tensor, 262144 pairs),
+routing skew calibrated to maxvio ~ 1; the sweep adds maxvio ~ 0.5, 2, 4.
+value = token-expert pairs planned and dispatched per second,
+N / (plan time + dispatch time), at the headline point.  The JSON also carries
+group-GEMM TFLOP/s and reduce_grad GB/s, every stage's roofline (the longest
+stage's as `roofline`), the backward of the data path (combine backward,
+dgrad, dispatch backward) as `next_rows`, the sweep and its flatness, the other
+workloads timed after the headline one (`other_workloads`: the mid sweep with
+the backward workload's point, the mid gated FFN, the routing-stress
+plan + dispatch), and the CPU oracle's plan + dispatch rate on a bounded sample.
 
     python bench.py --stats-md run_kernel_stats.csv          (rocprofv3 summary -> markdown)
     python bench.py --traffic-md fetch.csv write.csv         (counter runs -> per-stage HBM bytes)
@@ -49,13 +53,16 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="mid", choices=sorted(WORKLOAD_KEYS))
+    ap.add_argument("--workload", default="large", choices=sorted(WORKLOAD_KEYS))
     ap.add_argument("--maxvio", type=float, default=None, help="target maxvio of the headline point")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--forward-only", action="store_true")
-    ap.add_argument("--no-ffn", action="store_true", help="skip the full gated expert FFN in next_rows")
+    ap.add_argument("--no-ffn", action="store_true", help="skip the full gated expert FFN on the mid dims")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time only the headline workload (by default the large run is followed by the mid sweep "
+                         "with the backward workload's point, the mid FFN and the routing-stress workload)")
     ap.add_argument("--stats-md", metavar="CSV",
                     help="print a markdown table of the library kernels in a rocprofv3 kernel_stats.csv; no GPU")
     ap.add_argument("--traffic-md", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -254,7 +261,7 @@ def time_ffn(wl, seed, alpha, steps, warmup):
     return out
 
 
-def algorithmic(wl, stats, slot_expert_np, L):
+def algorithmic(wl, stats, slot_expert_np, L, cu=None):
     """Algorithmic work per launch of each stage: bytes for the bandwidth-bound stages (every input byte
     read once, every output byte written once), flops for the two GEMMs plus the least HBM bytes they can
     move (each operand read once, each output written once; wgrad's float32 gradient read and written)."""
@@ -265,7 +272,7 @@ def algorithmic(wl, stats, slot_expert_np, L):
     if wl.Hp is not None:
         Hp = wl.Hp
         G = wl.E + wl.B
-        cu = L.cu_seqlens.cpu().numpy().reshape(wl.R, G + 1)
+        cu = (L.cu_seqlens.cpu().numpy() if cu is None else np.asarray(cu)).reshape(wl.R, G + 1)
         rows = np.diff(cu, axis=1)  # [R, E+B] rows per (rank, group)
         home_used = int((rows[:, :wl.E].sum(axis=0) > 0).sum())
         slots_used = int((rows[:, wl.E:] > 0).sum())
@@ -375,25 +382,43 @@ def load_traffic(wl, target):
 
 
 def stage_roofline(name, alg, ms, traffic, f32, mfma=None):
+    """Roofline entry of one stage.  A bandwidth stage is bound by HBM: achieved = its algorithmic bytes per
+    launch over the launch's duration.  A GEMM stage is bound by the larger of its two floors: its flops at
+    the MFMA peak (fp32 vector peak for float32), or its least bytes (each operand read once, each output
+    written once; wgrad's float32 gradient read and written) at the HBM peak; `achieved` is then the flop
+    rate or the least-bytes rate accordingly, and both floors are given."""
     gemm = name in GEMM_STAGES
+    t = traffic.get(name)
+    secs = ms * 1e-3
     if gemm:
-        bound, unit = ("alu", "TFLOP/s") if f32 else ("mfma", "TFLOP/s")
-        peak = MFMA_F32_VECTOR_TFLOPS if f32 else MFMA_BF16_PEAK_TFLOPS
-        achieved = alg[name] / (ms * 1e-3) / 1e12
-        per = f"{alg[name]:.4g} FLOP (2*N*H*H')"
+        cpeak = MFMA_F32_VECTOR_TFLOPS if f32 else MFMA_BF16_PEAK_TFLOPS
+        least = alg.get(name + "_min_bytes")
+        floor_c = alg[name] / (cpeak * 1e12)
+        floor_m = (least or 0) / (HBM_PEAK_GBS * 1e9)
+        tflops = alg[name] / secs / 1e12
+        if floor_m > floor_c:
+            bound, unit, peak = "hbm", "GB/s", HBM_PEAK_GBS
+            achieved = least / secs / 1e9
+            per = f"{least:.4g} B (least bytes; {alg[name]:.4g} FLOP = 2*N*H*H')"
+        else:
+            bound, unit, peak = ("alu" if f32 else "mfma"), "TFLOP/s", cpeak
+            achieved = tflops
+            per = f"{alg[name]:.4g} FLOP (2*N*H*H')"
     else:
         bound, unit, peak = "hbm", "GB/s", HBM_PEAK_GBS
-        achieved = alg[name] / (ms * 1e-3) / 1e9
+        achieved = alg[name] / secs / 1e9
         per = f"{alg[name]:.4g} B"
-    t = traffic.get(name)
     r = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
          "frac": round(achieved / peak, 4), "traffic": t, "avg_launch_ms": round(ms, 4),
          "algorithmic_per_launch": per}
-    least = alg.get(name + "_min_bytes", alg[name] if not gemm else None)
     if gemm:
+        r["tflops"] = round(tflops, 2)
+        r["frac_of_mfma_peak"] = round(tflops / cpeak, 4)
+        r["floors_ms"] = {"compute": round(floor_c * 1e3, 4), "hbm": round(floor_m * 1e3, 4)}
         r["least_bytes_per_launch"] = least
-    if t:
-        r["traffic_over_least_bytes"] = round(t / least, 3)
+    least_b = least if gemm else alg[name]
+    if t and least_b:
+        r["traffic_over_least_bytes"] = round(t / least_b, 3)
     if gemm and not f32:
         r["mfma_util"] = (mfma or {}).get(name)  # from the committed counter summary, None once stale
     return r
@@ -599,50 +624,31 @@ def load_ffn_traffic(wl):
     return out
 
 
-def cpu_sample_tokens(wl):
-    """Tokens per rank of the oracle's timed sample: the whole workload while its GEMM work is at most
-    the mid workload's (2*N*H*H' with N = 196608, H = 2048, H' = 1408; 10-20 s of float64 BLAS on 8-16
-    cores), else as many tokens as give that much work; 640 tokens per rank for routing-only workloads."""
-    if wl.Hp is None:
-        return max(1, min(wl.S, 640))
-    return max(1, min(wl.S, 196608 * 2048 * 1408 // (wl.H * wl.Hp) // (wl.R * wl.K)))
-
-
-def cpu_baseline(wl, seed, alpha, tokens_per_rank):
-    """The oracle as it stands, on a bounded sample: the same routing recipe with S' tokens per rank and
-    the workload's full E, B, H, H'; pairs/s = sampled pairs / oracle time of the whole step."""
+def cpu_baseline(wl, seed, alpha, tokens_per_rank=512, min_seconds=10.0, max_reps=60):
+    """The oracle as it stands, on the metric's first term: plan + dispatch of a bounded sample of the
+    workload (the same routing recipe and skew with S' tokens per rank, the full E, B and H), repeated
+    until about `min_seconds` of oracle work; pairs/s = pairs planned and dispatched / oracle time.  The
+    oracle's planner and permute are plain single-threaded numpy."""
     import numpy as np
 
     from oracle import layer as olayer
     from oracle import planner as oplanner
     from synthetic.router import router_output
-    sw = wl.with_dims(S=tokens_per_rank)
-    idx, gates = router_output(sw.R, sw.S, sw.E, sw.K, seed, alpha=alpha, zipf_s=sw.zipf_s)
-    rng = np.random.default_rng(seed)
-    X = rng.standard_normal((sw.R, sw.S, sw.H))
-    if sw.Hp is not None:  # inputs are drawn before the clock starts: only oracle work is timed
-        W = rng.standard_normal((sw.E, sw.H, sw.Hp)) / np.sqrt(sw.H)
-        dY = rng.standard_normal((sw.N, sw.Hp))
-    t0 = time.perf_counter()
-    p = oplanner.plan(idx, sw.E, sw.B)
-    Xp = olayer.dispatch(X, p.dest_idx)
-    if sw.Hp is not None:
-        Ws = olayer.prefetch(W, p.slot_expert)
-        Yp = olayer.group_gemm(Xp, W, Ws, p.cu_seqlens, sw.P)
-        olayer.combine(Yp, p.dest_idx, gates)
-        dWh = np.zeros_like(W)
-        dWs = np.zeros((sw.R, sw.B, sw.H, sw.Hp))
-        olayer.wgrad(Xp, dY, p.cu_seqlens, sw.P, dWh, dWs)
-        olayer.reduce_grad(p.slot_expert, dWh, dWs)
-    t = time.perf_counter() - t0
-    try:
-        import threadpoolctl
-        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
-    return {"value": sw.N / t, "unit": "pairs/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"whole step (plan, dispatch, prefetch, group GEMM, combine, wgrad, reduce_grad) on the same "
-                      f"recipe with S={sw.S} tokens per rank ({sw.N} pairs), full E/B/H/H', float64; {t:.1f} s"}
+    sw = wl.with_dims(S=min(wl.S, tokens_per_rank))
+    idx, _ = router_output(sw.R, sw.S, sw.E, sw.K, seed, alpha=alpha, zipf_s=sw.zipf_s)
+    X = np.random.default_rng(seed).standard_normal((sw.R, sw.S, sw.H))  # drawn before the clock starts
+    spent, reps = 0.0, 0
+    while reps < max_reps and (reps == 0 or spent < min_seconds):
+        t0 = time.perf_counter()
+        p = oplanner.plan(idx, sw.E, sw.B)
+        Xp = olayer.dispatch(X, p.dest_idx)
+        spent += time.perf_counter() - t0
+        reps += 1
+        del Xp
+    return {"value": sw.N * reps / spent, "unit": "pairs/s", "cores": 1, "kind": "oracle",
+            "sample": f"oracle plan + dispatch of the {wl.name} recipe with S={sw.S} tokens per rank ({sw.N} "
+                      f"pairs, full E={sw.E}, B={sw.B}, H={sw.H}, float64 rows), {reps} passes, {spent:.1f} s; "
+                      f"single-threaded numpy"}
 
 
 def hot_rank_factor(idx, wl):
@@ -715,6 +721,118 @@ def calibration_copy():
     torch.cuda.synchronize()
 
 
+SWEEPS = {"mid": (1.0, [0.0, 1.0, 2.0, 3.0]), "large": (1.0, [0.5, 1.0, 2.0, 4.0])}
+FORWARD_STAGES = ("plan", "dispatch", "prefetch", "group_gemm", "combine")
+
+
+def run_points(wl, L, backward, points, head_target, steps, warmup, seed, alpha_of):
+    """Times the step at each maxvio target (the headline point with `steps` steps, the others with half)."""
+    import torch
+
+    from synthetic.router import measured_maxvio
+    results = {}
+    for tgt in points:
+        alpha = alpha_of(wl, tgt)
+        idx, _ = load_inputs(L, wl, seed, alpha)
+        ms, stages = time_steps(L, backward, steps if tgt == head_target else max(5, steps // 2), warmup)
+        torch.cuda.synchronize()
+        stats = L.stats.cpu().numpy()
+        slots = L.slot_expert.cpu().numpy()
+        results[tgt] = dict(alpha=alpha, maxvio=float(L.maxvio.item()), ms=ms, stages=stages,
+                            stats=stats.tolist(), slots=slots, maxvio_host=measured_maxvio(idx, wl.E),
+                            hot_rank=hot_rank_factor(idx, wl), cu=L.cu_seqlens.cpu().numpy())
+        log(f"{wl.name} maxvio target {tgt}: measured {results[tgt]['maxvio']:.3f}, {ms:.3f} ms/step, "
+            f"stages {stages}")
+    return results
+
+
+def sweep_summary(wl, L, results, points):
+    """Per sweep point: stage times, forward time, copies, each stage's roofline fraction at that point
+    (prefetch and reduce_grad bytes follow its copies); flatness of every point against the lowest-maxvio one."""
+    sweep = []
+    for tgt in points:
+        r = results[tgt]
+        fwd = sum(r["stages"].get(n, 0.0) for n in FORWARD_STAGES)
+        alg_p = algorithmic(wl, r["stats"], r["slots"], L, cu=r["cu"])
+        frac_p = {n: stage_roofline(n, alg_p, ms_n, {}, wl.dtype == "f32")["frac"]
+                  for n, ms_n in r["stages"].items() if alg_p.get(n)}
+        sweep.append({"maxvio_target": tgt, "maxvio": round(r["maxvio"], 4), "ms_per_step": round(r["ms"], 4),
+                      "forward_ms": round(fwd, 4), "copies_slotted_direct": r["stats"][:3],
+                      "hot_rank_factor": round(r["hot_rank"], 4),
+                      "plan_dispatch_pairs_per_s": round(wl.N / ((r["stages"]["plan"] + r["stages"]["dispatch"]) * 1e-3)),
+                      "stages_ms": {k: round(v, 4) for k, v in r["stages"].items()},
+                      "roofline_frac": frac_p})
+    sweep.sort(key=lambda x: (x["maxvio_target"] is None, x["maxvio_target"]))
+    flat = None
+    if len(sweep) > 1:  # every point against the lowest-maxvio point: within +-10% is flat
+        f0, s0 = sweep[0]["forward_ms"], sweep[0]["ms_per_step"]
+        fr = [round(x["forward_ms"] / f0 - 1, 4) for x in sweep]
+        sr = [round(x["ms_per_step"] / s0 - 1, 4) for x in sweep]
+        flat = {"reference_maxvio": sweep[0]["maxvio"], "forward_rel": fr, "step_rel": sr,
+                "forward_within_10pct": all(abs(v) <= 0.10 for v in fr),
+                "step_within_10pct": all(abs(v) <= 0.10 for v in sr)}
+    return sweep, flat
+
+
+def point_rooflines(wl, L, r, traffic=None, mfma=None):
+    alg = algorithmic(wl, r["stats"], r["slots"], L, cu=r["cu"])
+    return alg, {n: stage_roofline(n, alg, r["stages"][n], traffic or {}, wl.dtype == "f32", mfma)
+                 for n in r["stages"]}
+
+
+def extra_workloads(args, alpha_of, no_ffn):
+    """The other workloads of the benchmark, each timed the same way after the headline one (its buffers
+    freed first): the mid sweep (maxvio ~ 0, 1, 3) together with the backward workload's point (mid dims,
+    maxvio ~ 2: wgrad and reduce_grad), the full gated FFN on the mid dims, and the routing-stress workload
+    (plan + dispatch)."""
+    import torch
+
+    from synthetic import WORKLOADS
+    out = {}
+    wl = WORKLOADS["mid_fwd"]
+    head, pts = SWEEPS["mid"]
+    log(f"extra workload: {wl.description}")
+    L = make_layer(wl, True)
+    res = run_points(wl, L, True, [head] + [t for t in pts if t != head], head, args.steps, args.warmup, args.seed,
+                     alpha_of)
+    sweep, flat = sweep_summary(wl, L, res, [head] + [t for t in pts if t != head])
+    _, rl1 = point_rooflines(wl, L, res[head], load_traffic(wl, head), load_mfma(wl, head))
+    h = res[head]["stages"]
+    out["mid_fwd"] = {
+        "workload": wl.description, "maxvio_target": head, "maxvio": round(res[head]["maxvio"], 4),
+        "plan_dispatch_pairs_per_s": round(wl.N / ((h["plan"] + h["dispatch"]) * 1e-3)),
+        "group_gemm_tflops": rl1["group_gemm"]["tflops"], "rooflines": rl1, "sweep": [x for x in sweep
+                                                                                    if x["maxvio_target"] != 2.0],
+        "sweep_flatness": sweep_summary(wl, L, res, [t for t in pts if t != 2.0])[1]}
+    wb = WORKLOADS["mid_bwd"]
+    _, rl2 = point_rooflines(wb, L, res[2.0])
+    out["mid_bwd"] = {"workload": wb.description, "maxvio_target": 2.0, "maxvio": round(res[2.0]["maxvio"], 4),
+                      "copies_slotted_direct": res[2.0]["stats"][:3],
+                      "wgrad": rl2["wgrad"], "reduce_grad": rl2["reduce_grad"]}
+    out["mid_sweep_with_backward_point"] = {"sweep": sweep, "sweep_flatness": flat}
+    del L
+    torch.cuda.empty_cache()
+    if not no_ffn:
+        log("full gated expert FFN (forward + backward) on the mid dims")
+        out["ffn_mid"] = time_ffn(wl, args.seed, alpha_of(wl, head), max(3, args.steps // 4), 2)
+        out["ffn_mid"]["workload"] = (f"gate|up [E+B, {wl.H}, {2 * wl.Hp}], swiglu, down [E+B, {wl.Hp}, "
+                                      f"{wl.H}] on the mid routing at maxvio ~ {head}")
+    ws = WORKLOADS["plan_stress"]
+    log(f"extra workload: {ws.description}")
+    L = make_layer(ws, False)
+    res = run_points(ws, L, False, [None], None, args.steps, args.warmup, args.seed, alpha_of)
+    r = res[None]
+    _, rls = point_rooflines(ws, L, r)
+    out["plan_stress"] = {"workload": ws.description, "maxvio": round(r["maxvio"], 4),
+                          "copies_slotted_direct": r["stats"][:3], "hot_rank_factor": round(r["hot_rank"], 4),
+                          "plan_dispatch_pairs_per_s": round(ws.N / ((r["stages"]["plan"] + r["stages"]["dispatch"])
+                                                                     * 1e-3)),
+                          "plan_ms": round(r["stages"]["plan"], 4), "dispatch": rls["dispatch"]}
+    del L
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -725,15 +843,12 @@ def main():
 
     wl = WORKLOADS[WORKLOAD_KEYS[args.workload]]
     backward = wl.Hp is not None and not args.forward_only
-    if args.workload == "mid":
-        head_target = 1.0 if args.maxvio is None else args.maxvio
-        sweep_targets = [0.0, 1.0, 2.0, 3.0]
-    elif args.workload == "large":
-        head_target = 1.0 if args.maxvio is None else args.maxvio
-        sweep_targets = [0.5, 1.0, 2.0, 4.0]
+    if args.workload in SWEEPS:
+        head_target, sweep_targets = SWEEPS[args.workload]
+        if args.maxvio is not None:
+            head_target = args.maxvio
     else:
-        head_target = None
-        sweep_targets = []
+        head_target, sweep_targets = None, []
     if args.stats_md:
         print(stats_markdown(args.stats_md))
         return
@@ -760,25 +875,23 @@ def main():
         print("```")
         return
 
-    import numpy as np  # noqa: F401
     import torch
 
     from synthetic.calibrate import alpha_for
-    from synthetic.router import measured_maxvio
 
-    def alpha_of(target):
-        if wl.zipf_s is not None:
+    def alpha_of(w, target):
+        if w.zipf_s is not None:
             return 0.0
         if target is None:
-            return wl.alpha or 0.0
-        key_wl = WORKLOADS["mid_bwd"] if (args.workload == "mid" and target == 2.0) else wl
+            return w.alpha or 0.0
+        key_wl = WORKLOADS["mid_bwd"] if (w.name == "mid_fwd" and target == 2.0) else w
         return alpha_for(key_wl, args.seed, target)
 
     if args.ffn_only:
         if wl.Hp is None:
             raise SystemExit("--ffn-only needs a workload with H'")
         if args.profile_pass:
-            F, calls = make_ffn(wl, args.seed, alpha_of(head_target))
+            F, calls = make_ffn(wl, args.seed, alpha_of(wl, head_target))
             for _ in range(1 + args.steps):
                 for _, f in calls:
                     f()
@@ -786,12 +899,12 @@ def main():
             calibration_copy()
             log("profile pass done: FFN passes, then a 1 GiB copy")
         else:
-            print(json.dumps({"ffn": time_ffn(wl, args.seed, alpha_of(head_target), args.steps, args.warmup)}))
+            print(json.dumps({"ffn": time_ffn(wl, args.seed, alpha_of(wl, head_target), args.steps, args.warmup)}))
         return
     log(f"workload {wl.description}; building buffers")
     L = make_layer(wl, backward)
     if args.profile_pass:
-        load_inputs(L, wl, args.seed, alpha_of(head_target))
+        load_inputs(L, wl, args.seed, alpha_of(wl, head_target))
         if backward:
             L.dout.normal_()
         for _ in range(1 + args.steps):
@@ -801,93 +914,67 @@ def main():
         calibration_copy()
         log("profile pass done: stages", [n for n, _ in stage_calls(L, backward)], "then a 1 GiB copy")
         return
-    results = {}
     points = [head_target] + ([t for t in sweep_targets if t != head_target] if not args.no_sweep else [])
-    for tgt in points:
-        alpha = alpha_of(tgt)
-        idx, _ = load_inputs(L, wl, args.seed, alpha)
-        ms, stages = time_steps(L, backward, args.steps if tgt == head_target else max(5, args.steps // 2),
-                                args.warmup)
-        torch.cuda.synchronize()
-        stats = L.stats.cpu().numpy()
-        slots = L.slot_expert.cpu().numpy()
-        results[tgt] = dict(alpha=alpha, maxvio=float(L.maxvio.item()), ms=ms, stages=stages,
-                            stats=stats.tolist(), slots=slots, maxvio_host=measured_maxvio(idx, wl.E),
-                            hot_rank=hot_rank_factor(idx, wl))
-        log(f"maxvio target {tgt}: measured {results[tgt]['maxvio']:.3f}, {ms:.3f} ms/step, stages {stages}")
+    results = run_points(wl, L, backward, points, head_target, args.steps, args.warmup, args.seed, alpha_of)
 
     h = results[head_target]
-    alg = algorithmic(wl, h["stats"], h["slots"], L)
+    traffic = load_traffic(wl, head_target)
+    mfma = load_mfma(wl, head_target)
+    alg, rooflines = point_rooflines(wl, L, h, traffic, mfma)
     st = h["stages"]
-    comp = {"plan_dispatch_pairs_per_s": wl.N / ((st["plan"] + st["dispatch"]) * 1e-3),
-            "plan_ms": st["plan"], "dispatch_GBs": alg["dispatch"] / (st["dispatch"] * 1e-3) / 1e9}
+    value = wl.N / ((st["plan"] + st["dispatch"]) * 1e-3)
+    comp = {"plan_dispatch_pairs_per_s": value, "plan_ms": st["plan"],
+            "dispatch_GBs": alg["dispatch"] / (st["dispatch"] * 1e-3) / 1e9}
     if wl.Hp is not None:
         comp["group_gemm_tflops"] = alg["group_gemm"] / (st["group_gemm"] * 1e-3) / 1e12
         comp["combine_GBs"] = alg["combine"] / (st["combine"] * 1e-3) / 1e9
         comp["prefetch_GBs"] = alg["prefetch"] / (st["prefetch"] * 1e-3) / 1e9 if alg["prefetch"] else None
+        comp["forward_ms"] = sum(st[n] for n in FORWARD_STAGES)
         if backward:
             comp["wgrad_tflops"] = alg["wgrad"] / (st["wgrad"] * 1e-3) / 1e12
             comp["reduce_grad_GBs"] = (alg["reduce_grad"] / (st["reduce_grad"] * 1e-3) / 1e9
                                        if alg["reduce_grad"] else None)
-    traffic = load_traffic(wl, head_target)
-    mfma = load_mfma(wl, head_target)
-    rooflines = {n: stage_roofline(n, alg, st[n], traffic, wl.dtype == "f32", mfma) for n in st}
     next_rows = None
     if backward:
         load_inputs(L, wl, args.seed, h["alpha"])  # the headline routing again (the sweep moved it)
         nx = time_next_rows(L, args.steps, args.warmup)
         log(f"backward of the data path: {nx}")
         next_rows = {n: stage_roofline(n, alg, nx[n], traffic, wl.dtype == "f32", mfma) for n in nx}
-        if wl.dtype == "bf16" and not args.no_ffn:
-            log("full gated expert FFN (forward + backward)")
-            next_rows["ffn"] = time_ffn(wl, args.seed, h["alpha"], max(3, args.steps // 4), 2)
-            next_rows["ffn"]["workload"] = (f"gate|up [E+B, {wl.H}, {2 * wl.Hp}], swiglu, down [E+B, {wl.Hp}, "
-                                            f"{wl.H}] on the same routing")
     dominant = max(st, key=lambda n: st[n])
     roofline = dict(rooflines[dominant], stage=dominant)
+    sweep, flat = sweep_summary(wl, L, results, points)
+    vendor = vendor_gemm_tflops(wl) if (wl.Hp is not None and wl.dtype == "bf16") else None
+    del L
+    torch.cuda.empty_cache()
+
+    extras = None
+    if args.workload == "large" and not args.no_extras:
+        extras = extra_workloads(args, alpha_of, args.no_ffn)
+        comp["stress_plan_dispatch_pairs_per_s"] = extras["plan_stress"]["plan_dispatch_pairs_per_s"]
+        comp["stress_dispatch_GBs"] = extras["plan_stress"]["dispatch"]["achieved"]
+        comp["mid_plan_dispatch_pairs_per_s"] = extras["mid_fwd"]["plan_dispatch_pairs_per_s"]
+        comp["mid_group_gemm_tflops"] = extras["mid_fwd"]["group_gemm_tflops"]
+        comp["backward_cfg_wgrad_tflops"] = extras["mid_bwd"]["wgrad"]["tflops"]
+        comp["backward_cfg_reduce_grad_GBs"] = extras["mid_bwd"]["reduce_grad"]["achieved"]
 
     cpu = None
     if not args.no_cpu_baseline:
-        log("timing the CPU oracle on a bounded sample")
-        cpu = cpu_baseline(wl, args.seed, h["alpha"], tokens_per_rank=cpu_sample_tokens(wl))
+        log("timing the CPU oracle's plan + dispatch on a bounded sample")
+        cpu = cpu_baseline(wl, args.seed, h["alpha"])
 
-    sweep = []
-    for tgt in points:
-        r = results[tgt]
-        fwd = sum(r["stages"].get(n, 0.0) for n in ("plan", "dispatch", "prefetch", "group_gemm", "combine"))
-        # each stage's roofline fraction at this point (prefetch and reduce_grad bytes follow its copies)
-        alg_p = algorithmic(wl, r["stats"], r["slots"], L)
-        frac_p = {n: stage_roofline(n, alg_p, ms_n, {}, wl.dtype == "f32")["frac"]
-                  for n, ms_n in r["stages"].items() if alg_p.get(n)}
-        sweep.append({"maxvio_target": tgt, "maxvio": round(r["maxvio"], 4), "ms_per_step": round(r["ms"], 4),
-                      "forward_ms": round(fwd, 4), "copies_slotted_direct": r["stats"][:3],
-                      "hot_rank_factor": round(r["hot_rank"], 4),
-                      "stages_ms": {k: round(v, 4) for k, v in r["stages"].items()},
-                      "roofline_frac": frac_p})
-    sweep.sort(key=lambda x: (x["maxvio_target"] is None, x["maxvio_target"]))
-    flat = None
-    if len(sweep) > 1:  # every point against the lowest-maxvio point: within +-10% is flat
-        f0, s0 = sweep[0]["forward_ms"], sweep[0]["ms_per_step"]
-        fr = [round(x["forward_ms"] / f0 - 1, 4) for x in sweep]
-        sr = [round(x["ms_per_step"] / s0 - 1, 4) for x in sweep]
-        flat = {"reference_maxvio": sweep[0]["maxvio"], "forward_rel": fr, "step_rel": sr,
-                "forward_within_10pct": all(abs(v) <= 0.10 for v in fr),
-                "step_within_10pct": all(abs(v) <= 0.10 for v in sr)}
-
-    log("timing the runtime's 1 GiB device copy and the vendor GEMM (reference rates)")
+    log("timing the runtime's 1 GiB device copy (reference rate)")
     copy_gbs = runtime_copy_gbs()
-    vendor = vendor_gemm_tflops(wl) if (wl.Hp is not None and wl.dtype == "bf16") else None
     if vendor:
         for n, key in (("group_gemm", "fwd"), ("dgrad", "fwd"), ("wgrad", "wgrad")):
             for entry in [rooflines.get(n), (next_rows or {}).get(n)] + ([roofline] if roofline.get("stage") == n else []):
                 if entry:
-                    entry["frac_of_vendor_gemm"] = round(entry["achieved"] / vendor[key], 4)
-    for entry in list(rooflines.values()) + [roofline] + [v for k, v in (next_rows or {}).items() if k != "ffn"]:
-        if entry.get("unit") == "GB/s":
+                    entry["frac_of_vendor_gemm"] = round(entry["tflops"] / vendor[key], 4)
+    for entry in list(rooflines.values()) + [roofline] + list((next_rows or {}).values()):
+        if entry.get("unit") == "GB/s" and entry.get("bound") == "hbm" and "tflops" not in entry:
             entry["frac_of_runtime_copy"] = round(entry["achieved"] / copy_gbs, 4)
     line = {
         "metric": "token-expert pairs/s planned+dispatched; group-GEMM TFLOP/s; reduce_grad GB/s",
-        "value": wl.N / (h["ms"] * 1e-3),
+        "value": value,
         "unit": "pairs/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(h["ms"], 4),
@@ -895,7 +982,8 @@ def main():
         "dtype": "bf16" if wl.dtype == "bf16" else "f32",
         "data": "synthetic (seeded router skew, N(0,1) activations, N(0,1/H) weights)",
         "config": {"workload": f"{wl.name}: {wl.description}; step = "
-                               + ("forward + backward" if backward else "forward"),
+                               + ("forward + backward" if backward else "forward")
+                               + "; value = pairs / (plan + dispatch time)",
                    "R": wl.R, "E": wl.E, "B": wl.B, "S": wl.S, "K": wl.K, "H": wl.H, "Hp": wl.Hp,
                    "pairs_per_step": wl.N, "maxvio_target": head_target, "maxvio": round(h["maxvio"], 4),
                    "copies_slotted_direct": h["stats"][:3]},
@@ -908,14 +996,13 @@ def main():
                             "vendor_gemm_fwd_TFLOPs": round(vendor["fwd"], 1) if vendor else None,
                             "vendor_gemm_wgrad_TFLOPs": round(vendor["wgrad"], 1) if vendor else None,
                             "note": "the HIP runtime's device copy of 1 GiB (read + write), HIP events; a GB/s "
-                                    "stage's frac_of_runtime_copy is its rate over this (above 1: faster than "
-                                    "the runtime's copy). A one-shot 16-byte-per-thread copy kernel measured "
-                                    "about 6.5 TB/s (81% of 8 TB/s), the practical HBM ceiling. vendor_gemm_*: "
+                                    "stage's frac_of_runtime_copy is its rate over this. vendor_gemm_*: "
                                     "hipBLASLt (torch.matmul, bf16) on the same FLOPs as R dense GEMMs, "
                                     "[P,H]x[H,H'] and [H,P]x[P,H']; a GEMM stage's frac_of_vendor_gemm is its "
-                                    "rate over that."},
+                                    "flop rate over that."},
         "sweep": sweep,
         "sweep_flatness": flat,
+        "other_workloads": extras,
     }
     print(json.dumps(line), flush=True)
 

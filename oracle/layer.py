@@ -60,22 +60,26 @@ def row_group(cu_seqlens: np.ndarray, P: int, rows: np.ndarray):
     return ranks, groups
 
 
-def group_gemm(Xp, W_home, W_slots, cu_seqlens, P: int, rows=None) -> np.ndarray:
+def group_gemm(Xp, W_home, W_slots, cu_seqlens, P: int, rows=None, ranks=None) -> np.ndarray:
     """Yp[rows of group g on rank r] = Xp[those rows] @ W_r[g] ([P2] "Memory contract": VM group GEMM).
 
     With ``rows`` given, returns only those output rows (Xp must then be the full
-    buffer or any array indexable by the row ids).
+    buffer or any array indexable by the row ids).  With ``ranks`` given, returns
+    the whole buffers of those ranks, one after the other ([len(ranks)*P, H']).
     """
     R = cu_seqlens.shape[0]
     G = cu_seqlens.shape[1] - 1
     Hp = W_home.shape[2]
     if rows is None:
-        Y = np.zeros((Xp.shape[0], Hp), dtype=np.float64)
-        for r in range(R):
+        rs = range(R) if ranks is None else list(ranks)
+        Y = np.zeros((len(rs) * P, Hp), dtype=np.float64)
+        for i, r in enumerate(rs):
             for g in range(G):
                 a, b = r * P + cu_seqlens[r, g], r * P + cu_seqlens[r, g + 1]
                 if b > a:
-                    Y[a:b] = Xp[a:b].astype(np.float64) @ rank_weight(W_home, W_slots, r, g).astype(np.float64)
+                    o = i * P + cu_seqlens[r, g]
+                    Y[o:o + b - a] = (np.asarray(Xp[a:b], dtype=np.float64)
+                                      @ np.asarray(rank_weight(W_home, W_slots, r, g), dtype=np.float64))
         return Y
     ranks, groups = row_group(cu_seqlens, P, rows)
     Y = np.zeros((len(rows), Hp), dtype=np.float64)
@@ -179,22 +183,26 @@ def combine_backward(dout: np.ndarray, Yp: np.ndarray, dest_idx: np.ndarray, gat
     return dYp, dgate.reshape(R, S, K)
 
 
-def group_gemm_dgrad(dYp, W_home, W_slots, cu_seqlens, P: int, rows=None) -> np.ndarray:
+def group_gemm_dgrad(dYp, W_home, W_slots, cu_seqlens, P: int, rows=None, ranks=None) -> np.ndarray:
     """dXp[rows of group g on rank r] = dYp[those rows] @ W_r[g]^T: the gradient of the VM group GEMM
     with respect to its input, through the same groups and the same weight rows (home or slot).
 
-    With ``rows`` given, returns only those output rows.
+    With ``rows`` given, returns only those output rows; with ``ranks`` given, the whole buffers of
+    those ranks, one after the other ([len(ranks)*P, H]).
     """
     R = cu_seqlens.shape[0]
     G = cu_seqlens.shape[1] - 1
     H = W_home.shape[1]
     if rows is None:
-        dX = np.zeros((dYp.shape[0], H), dtype=np.float64)
-        for r in range(R):
+        rs = range(R) if ranks is None else list(ranks)
+        dX = np.zeros((len(rs) * P, H), dtype=np.float64)
+        for i, r in enumerate(rs):
             for g in range(G):
                 a, b = r * P + cu_seqlens[r, g], r * P + cu_seqlens[r, g + 1]
                 if b > a:
-                    dX[a:b] = dYp[a:b].astype(np.float64) @ rank_weight(W_home, W_slots, r, g).astype(np.float64).T
+                    o = i * P + cu_seqlens[r, g]
+                    dX[o:o + b - a] = (np.asarray(dYp[a:b], dtype=np.float64)
+                                       @ np.asarray(rank_weight(W_home, W_slots, r, g), dtype=np.float64).T)
         return dX
     ranks, groups = row_group(cu_seqlens, P, rows)
     dX = np.zeros((len(rows), H), dtype=np.float64)
@@ -271,18 +279,62 @@ def moe_forward(X, W_home, topk_idx, gates, tokens=None) -> np.ndarray:
     return out if tokens is not None else out.reshape(R, S, -1)
 
 
-def expert_weight_grad(X, dY_of_pair, topk_idx, E: int) -> np.ndarray:
-    """Plain expert weight gradient: dW[e] = sum over pairs (t,k) with expert e of x_t^T dy_(t,k)."""
+def expert_weight_grad(X, dY_of_pair, topk_idx, E: int, experts=None) -> np.ndarray:
+    """Plain expert weight gradient: dW[e] = sum over pairs (t,k) with expert e of x_t^T dy_(t,k).
+
+    ``experts`` restricts the result to those experts ([len(experts), H, H'], in that order); dY_of_pair
+    then needs only row indexing by pair ids.
+    """
     R, S, H = X.shape
     K = topk_idx.shape[2]
-    Xf = X.reshape(R * S, H).astype(np.float64)
+    Xf = X.reshape(R * S, H)
     ids = np.asarray(topk_idx).reshape(R * S * K)
-    dW = np.zeros((E, H, dY_of_pair.shape[1]), dtype=np.float64)
-    for e in range(E):
+    sel = range(E) if experts is None else list(experts)
+    dW = np.zeros((len(sel), H, dY_of_pair.shape[1]), dtype=np.float64)
+    for i, e in enumerate(sel):
         q = np.nonzero(ids == e)[0]
         if len(q):
-            dW[e] = Xf[q // K].T @ dY_of_pair[q].astype(np.float64)
+            dW[i] = np.asarray(Xf[q // K], dtype=np.float64).T @ np.asarray(dY_of_pair[q], dtype=np.float64)
     return dW
+
+
+def moe_forward_rows(Xt, W_home, ids, gates):
+    """moe_forward for a block of tokens given as rows: out[i] = sum over k ascending of
+    gate[i,k] * Xt[i] @ W[ids[i,k]], and the scale sum_k |gate[i,k] * Xt[i] @ W[ids[i,k]]| of that sum.
+
+    Each (i, k) term is one row of a matmul over the tokens that chose the same expert (each expert's
+    weights are read once); the terms are kept apart until the k-ascending sum.
+    """
+    Xt = np.asarray(Xt, dtype=np.float64)
+    ids = np.asarray(ids)
+    g = np.asarray(gates, dtype=np.float64)
+    n, K = ids.shape
+    terms = np.zeros((K, n, W_home.shape[2]), dtype=np.float64)
+    for e in np.unique(ids):
+        i, k = np.nonzero(ids == e)
+        terms[k, i] = g[i, k][:, None] * (Xt[i] @ np.asarray(W_home[e], dtype=np.float64))
+    out = terms[0].copy()
+    for k in range(1, K):
+        out += terms[k]
+    return out, np.abs(terms).sum(axis=0)
+
+
+def moe_input_grad_rows(dY_rows, W_home, ids):
+    """Gradient of the planned layer's input for a block of tokens, through dgrad and the permute's
+    backward: dX[i] = sum over k ascending of dY_rows[i,k] @ W[ids[i,k]]^T, where dY_rows[i,k] is the
+    gradient row of pair (i, k) in the dispatched buffer; also the scale sum_k |that term|.  One matmul
+    per expert over the pairs that chose it; terms kept apart until the k-ascending sum."""
+    dY_rows = np.asarray(dY_rows, dtype=np.float64)
+    ids = np.asarray(ids)
+    n, K = ids.shape
+    terms = np.zeros((K, n, W_home.shape[1]), dtype=np.float64)
+    for e in np.unique(ids):
+        i, k = np.nonzero(ids == e)
+        terms[k, i] = dY_rows[i, k] @ np.asarray(W_home[e], dtype=np.float64).T
+    out = terms[0].copy()
+    for k in range(1, K):
+        out += terms[k]
+    return out, np.abs(terms).sum(axis=0)
 
 
 def moe_backward(X, W_home, topk_idx, gates, dout):

@@ -4,7 +4,9 @@ The pages call their planner a near-optimal online integer program but do not
 state its objective ([P1] abstract; [P2] "Core technique").  The reading used
 here: a copy is an (expert e, rank d != home(e)) pair that carries at least one
 of e's pairs; minimise the number of copies subject to every rank holding
-exactly P pairs and every expert's T_e pairs being placed.  No slot cap.
+exactly P pairs and every expert's T_e pairs being placed; optionally also
+subject to a slot cap (every rank receives at most B distinct non-home
+experts, so that none is read directly from its home row).
 
 Method: try every set of allowed non-home edges, smallest sets first, and test
 each with a max-flow (source -> expert, capacity T_e; expert -> its home rank
@@ -52,8 +54,13 @@ def lower_bound(T, R, P) -> int:
     return int(max(np.sum(load > P), np.sum(load < P)))
 
 
-def min_copies(T, R: int, P: int, max_size: int | None = None) -> int:
-    """Smallest number of non-home (expert, rank) placements that balances every rank to exactly P."""
+def min_copies(T, R: int, P: int, max_size: int | None = None, slot_cap: int | None = None):
+    """Smallest number of non-home (expert, rank) placements that balances every rank to exactly P.
+
+    With ``slot_cap`` = B, only placements in which every rank receives at most B distinct non-home
+    experts count (each one then fits a prefetch slot: no direct reads); returns None when no such
+    placement exists.
+    """
     T = np.asarray(T, dtype=np.int64)
     E = len(T)
     per = E // R
@@ -63,6 +70,10 @@ def min_copies(T, R: int, P: int, max_size: int | None = None) -> int:
     top = len(cand) if max_size is None else max_size
     for size in range(0, top + 1):
         for edges in combinations(cand, size):
+            if slot_cap is not None and max(np.bincount([d for _, d in edges], minlength=R)) > slot_cap:
+                continue
             if _feasible(T, R, P, home, edges):
                 return size
+    if slot_cap is not None:
+        return None
     raise RuntimeError("no balancing placement within the size limit")

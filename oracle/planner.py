@@ -21,8 +21,15 @@ notes of the repository):
   * Canonical pair order is (expert, src rank, token, k); the flat pair id
     q = (src*S + token)*K + k is already in (src, token, k) order, so the order
     inside one expert is ascending q.
-  * Home-first: rank r walks its home experts in ascending order and keeps the
-    first P = S*K pairs of that list; the rest overflow.
+  * Home-first ("prefix" planner): rank r walks its home experts in ascending
+    order and keeps the first P = S*K pairs of that list; the rest overflow.
+  * Fewest copies ("mincopy" planner, the pages' planner minimises the
+    redundant experts it creates but does not print its program): an
+    overloaded rank sends its excess L_r - P out of as few of its experts as
+    possible -- its home experts largest first (equal counts: lower id first),
+    each overflowing in turn until the excess is covered -- and keeps the first
+    keep_e pairs of every expert.  Everything after the keep counts is the
+    same for both planners.
   * The overflow list is every overflow pair in ascending (expert, order); the
     deficits D_r = max(0, P - L_r) of underloaded ranks are filled from it in
     rank order, each deficit taking one contiguous cut.
@@ -89,8 +96,47 @@ def stable_order(ids: np.ndarray) -> np.ndarray:
     return out
 
 
-def plan(topk_idx: np.ndarray, E: int, B: int) -> Plan:
-    """Home-first prefix-sum plan for router output ``topk_idx`` [R, S, K]."""
+PLANNERS = ("prefix", "mincopy")
+
+
+def keep_counts(T: np.ndarray, R: int, P: int, planner: str = "prefix"):
+    """How many of each expert's pairs stay on its home rank, and L_r, the pairs whose expert lives on r.
+
+    prefix:  rank r walks its home experts in ascending order and keeps the first P pairs of that list.
+    mincopy: a rank with L_r > P must send out L_r - P pairs; it takes its home experts largest first
+             (equal counts: lower id first) and overflows each of them in turn, as much as is still
+             needed, so the excess leaves through the fewest experts; the last one may keep some pairs.
+    """
+    E = len(T)
+    per = E // R
+    keep = np.zeros(E, dtype=np.int64)
+    load = np.zeros(R, dtype=np.int64)
+    for r in range(R):
+        experts = list(range(r * per, (r + 1) * per))
+        load[r] = sum(int(T[e]) for e in experts)
+        if planner == "prefix":
+            before = 0  # pairs of r's lower-numbered home experts
+            for e in experts:
+                keep[e] = min(max(P - before, 0), T[e])
+                before += T[e]
+        elif planner == "mincopy":
+            excess = load[r] - P
+            for e in experts:
+                keep[e] = T[e]
+            for e in sorted(experts, key=lambda e: (-T[e], e)):
+                if excess <= 0:
+                    break
+                moved = min(int(T[e]), excess)
+                keep[e] = T[e] - moved
+                excess -= moved
+        else:
+            raise ValueError(f"unknown planner {planner!r}")
+    return keep, load
+
+
+def plan(topk_idx: np.ndarray, E: int, B: int, planner: str = "prefix") -> Plan:
+    """Balanced plan for router output ``topk_idx`` [R, S, K]: the home-first prefix planner, or with
+    planner="mincopy" the planner that sends each rank's excess out of the fewest experts."""
     topk_idx = np.asarray(topk_idx, dtype=np.int64)
     R, S, K = topk_idx.shape
     assert E % R == 0 and B >= 0
@@ -107,15 +153,9 @@ def plan(topk_idx: np.ndarray, E: int, B: int) -> Plan:
     # Step 2: canonical order inside each expert.
     order = stable_order(ids)
 
-    # Step 3: home-first keep counts.  L_r = pairs whose expert lives on r.
-    keep = np.zeros(E, dtype=np.int64)
-    load = np.zeros(R, dtype=np.int64)
-    for r in range(R):
-        before = 0  # pairs of r's lower-numbered home experts
-        for e in range(r * per, (r + 1) * per):
-            keep[e] = min(max(P - before, 0), T[e])
-            before += T[e]
-        load[r] = before
+    # Step 3: keep counts (which of each expert's pairs stay home: the first keep_e of its canonical
+    # list).  L_r = pairs whose expert lives on r.
+    keep, load = keep_counts(T, R, P, planner)
     over = T - keep
 
     # Step 4: the overflow list (ascending expert, then order) and the deficits.

@@ -71,3 +71,92 @@ def assert_sum_close(gpu, ref, scale, rel=1e-5, what="sum"):
 def bf16_round_np(a: np.ndarray) -> np.ndarray:
     """Round float64 values to bf16 (via torch, round-to-nearest-even) and return float64."""
     return torch.as_tensor(a, dtype=torch.float32).to(torch.bfloat16).float().numpy().astype(np.float64)
+
+
+# ------------------------------------------------------------------ lazy host views of generated inputs
+#
+# At the workloads' full sizes the float64 host copies of the inputs would be tens of GB, so the oracle
+# receives objects that fetch what it indexes.  They hold generator outputs (device tensors drawn by the
+# seeded generators, never written by the library) and the oracle's own index maps.
+
+class DeviceExperts:
+    """W_home[e] of a device weight tensor as float64 on the host, fetched when indexed (two cached)."""
+
+    def __init__(self, t: torch.Tensor):
+        self.t = t
+        self.shape = tuple(t.shape)
+        self._cache = {}
+
+    def __getitem__(self, e):
+        e = int(e)
+        if e not in self._cache:
+            if len(self._cache) >= 2:
+                self._cache.pop(next(iter(self._cache)))
+            self._cache[e] = np64(self.t[e])
+        return self._cache[e]
+
+
+class OracleSlots:
+    """W_slots[r, j] as the oracle's prefetch defines it: the home weights of slot_expert[r, j]."""
+
+    def __init__(self, W: DeviceExperts, slot_expert: np.ndarray):
+        self.W, self.slot = W, slot_expert
+
+    def __getitem__(self, rj):
+        r, j = rj
+        e = int(self.slot[r, j])
+        assert e >= 0, "read of an unused slot"
+        return self.W[e]
+
+
+class DispatchedRows:
+    """Xp as the oracle's dispatch defines it: row i is token src_of_row[i] // K of the device tensor X
+    ([R*S, H] view); rows are gathered on the device and returned as float64."""
+
+    def __init__(self, Xf: torch.Tensor, src_of_row: np.ndarray, K: int):
+        self.Xf, self.src, self.K = Xf, src_of_row, K
+        self.shape = (len(src_of_row), Xf.shape[1])
+
+    def __getitem__(self, rows):
+        tok = np.asarray(self.src[rows]) // self.K
+        return np64(self.Xf[torch.as_tensor(tok, device=self.Xf.device)])
+
+
+class DeviceRows:
+    """Rows of a device tensor (a generator output such as dY), fetched as float64 when indexed; with
+    `index`, item i is row index[i] of the tensor (e.g. the gradient row of pair i, index = dest_idx)."""
+
+    def __init__(self, t: torch.Tensor, index=None):
+        self.t = t
+        self.index = None if index is None else np.asarray(index)
+        n = t.shape[0] if index is None else len(self.index)
+        self.shape = (n,) + tuple(t.shape[1:])
+
+    def __getitem__(self, rows):
+        ids = np.arange(self.shape[0])[rows] if isinstance(rows, slice) else np.asarray(rows)
+        if self.index is not None:
+            ids = self.index[ids]
+        return np64(self.t[torch.as_tensor(ids, device=self.t.device)])
+
+
+class Guarded:
+    """A device buffer of `shape` inside a larger allocation whose guard regions before and after it hold a
+    fixed bit pattern; intact() tells whether anything wrote outside the buffer."""
+
+    PATTERN = {2: 0x5A5B, 4: 0x5A5B5C5D}
+
+    def __init__(self, shape, dtype, guard_bytes=64 * 1024):
+        es = torch.empty((), dtype=dtype).element_size()
+        self.g = guard_bytes // es
+        self.n = int(np.prod(shape))
+        self.buf = torch.empty(self.n + 2 * self.g, dtype=dtype, device=DEV)
+        self.view = self.buf[self.g:self.g + self.n].view(shape)
+        self.ity = {2: torch.int16, 4: torch.int32}[es]
+        self.pat = self.PATTERN[es]
+        self.buf[:self.g].view(self.ity).fill_(self.pat)
+        self.buf[self.g + self.n:].view(self.ity).fill_(self.pat)
+
+    def intact(self) -> bool:
+        lo = self.buf[:self.g].view(self.ity)
+        hi = self.buf[self.g + self.n:].view(self.ity)
+        return bool((lo == self.pat).all().item()) and bool((hi == self.pat).all().item())

@@ -8,8 +8,15 @@ from __future__ import annotations
 import numpy as np
 
 
-def check_plan_invariants(topk_idx, E, B, cu, slot_expert, dest_idx, src_of_row=None, stats=None):
-    """Invariants from the pages and the planner reading; raises AssertionError on the first violation."""
+def check_plan_invariants(topk_idx, E, B, cu, slot_expert, dest_idx, src_of_row=None, stats=None,
+                          planner="prefix"):
+    """Invariants from the pages and the planner reading; raises AssertionError on the first violation.
+
+    planner="prefix": every rank keeps the first min(P, L_r) pairs of its canonical home list.
+    planner="mincopy": every expert keeps a canonical prefix of its pairs, and an overloaded rank's
+    overflow leaves through its home experts largest first (equal counts: lower id first): in that
+    order the experts are wholly overflowed, then at most one partly, then kept whole.
+    """
     topk_idx = np.asarray(topk_idx, dtype=np.int64)
     R, S, K = topk_idx.shape
     P, N, per = S * K, R * S * K, E // R
@@ -62,11 +69,26 @@ def check_plan_invariants(topk_idx, E, B, cu, slot_expert, dest_idx, src_of_row=
             slot_es = [e for e, k in lst if k == "slot"]
             if slot_es:
                 assert max(slot_es) < min(e for e, k in lst if k == "direct"), "slots go to the lowest experts"
-    # home-first: rank r keeps the first min(P, L_r) pairs of its canonical home list
-    for r in range(R):
-        home_pairs = [q for e in range(r * per, (r + 1) * per) for q in np.nonzero(ids == e)[0]]
-        kept = [q for q in home_pairs if dest[q] // P == r]
-        assert kept == home_pairs[:min(P, len(home_pairs))], "home-first prefix property"
+    if planner == "prefix":  # home-first: rank r keeps the first min(P, L_r) pairs of its canonical home list
+        for r in range(R):
+            home_pairs = [q for e in range(r * per, (r + 1) * per) for q in np.nonzero(ids == e)[0]]
+            kept = [q for q in home_pairs if dest[q] // P == r]
+            assert kept == home_pairs[:min(P, len(home_pairs))], "home-first prefix property"
+    else:
+        assert planner == "mincopy"
+        for r in range(R):
+            experts = list(range(r * per, (r + 1) * per))
+            T = {e: int(np.sum(ids == e)) for e in experts}
+            kept_n = {}
+            for e in experts:
+                qs = list(np.nonzero(ids == e)[0])
+                kept = [q for q in qs if dest[q] // P == r]
+                assert kept == qs[:len(kept)], "every expert keeps a canonical prefix of its pairs"
+                kept_n[e] = len(kept)
+            assert sum(kept_n.values()) == min(P, sum(T.values())), "an overloaded rank keeps exactly P"
+            order = sorted(experts, key=lambda e: (-T[e], e))
+            state = [0 if kept_n[e] == 0 and T[e] > 0 else (2 if kept_n[e] == T[e] else 1) for e in order]
+            assert state == sorted(state) and state.count(1) <= 1, "overflow leaves through the largest experts"
     # contiguous cut: overflow pairs in canonical order go to non-decreasing ranks
     over = []
     for e in range(E):
@@ -81,14 +103,16 @@ def check_plan_invariants(topk_idx, E, B, cu, slot_expert, dest_idx, src_of_row=
     return True
 
 
-def list_plan(topk_idx, E, B):
+def list_plan(topk_idx, E, B, planner="prefix"):
     """Builds every rank's buffer by moving pair ids between Python lists.
 
     Rank r lists its home experts' pairs (ascending expert, then ascending pair
-    id) and keeps the first P; the leftovers of all ranks, concatenated in rank
-    order, are handed to the ranks below P in rank order; each receiving rank
-    gives its arrived experts slots in ascending order (home-row groups past B).
-    Returns (cu [R,E+B+1], slot_expert [R,B], dest [R,S,K]).
+    id) and keeps the first P (planner="mincopy": it strips its excess from the
+    tails of its experts' lists, the longest list first, equal lengths lower
+    expert first); the leftovers of all ranks, in rank order and ascending
+    expert within a rank, are handed to the ranks below P in rank order; each
+    receiving rank gives its arrived experts slots in ascending order (home-row
+    groups past B).  Returns (cu [R,E+B+1], slot_expert [R,B], dest [R,S,K]).
     """
     topk_idx = np.asarray(topk_idx, dtype=np.int64)
     R, S, K = topk_idx.shape
@@ -98,7 +122,17 @@ def list_plan(topk_idx, E, B):
     for r in range(R):
         mine = [(e, q) for e in range(r * per, (r + 1) * per) for q in range(N) if ids[q] == e]
         load[r] = len(mine)
-        kept[r], overflow = mine[:P], overflow + mine[P:]
+        if planner == "prefix":
+            kept[r], overflow = mine[:P], overflow + mine[P:]
+            continue
+        lists = {e: [(ee, q) for ee, q in mine if ee == e] for e in range(r * per, (r + 1) * per)}
+        strip = {e: 0 for e in lists}
+        excess = len(mine) - P
+        for e in sorted(lists, key=lambda e: (-len(lists[e]), e)):
+            strip[e] = max(0, min(len(lists[e]), excess))
+            excess -= strip[e]
+        kept[r] = [x for e in sorted(lists) for x in lists[e][:len(lists[e]) - strip[e]]]
+        overflow = overflow + [x for e in sorted(lists) for x in lists[e][len(lists[e]) - strip[e]:]]
     received = {}
     for d in range(R):
         need = max(0, P - load[d])

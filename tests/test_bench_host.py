@@ -224,3 +224,20 @@ def test_stage_roofline_fraction_and_algorithmic_bytes():
     assert abs(r["frac"] - r["achieved"] / bench.HBM_PEAK_GBS) < 1e-4
     g = bench.stage_roofline("group_gemm", alg, 1.0, {}, False)
     assert g["unit"] == "TFLOP/s" and abs(g["frac"] - (alg["group_gemm"] / 1e-3 / 1e12) / bench.MFMA_BF16_PEAK_TFLOPS) < 1e-4
+
+
+def test_gemm_roofline_takes_the_higher_floor():
+    # large wgrad: 7.7 TFLOP (3.08 ms at the MFMA peak) but 39.7 GB of least bytes (4.96 ms at 8 TB/s): HBM binds
+    alg = {"wgrad": 2 * 262144 * 7168 * 2048, "wgrad_min_bytes": 39.7e9}
+    r = bench.stage_roofline("wgrad", alg, 10.0, {}, False)
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == bench.HBM_PEAK_GBS
+    assert abs(r["achieved"] - 39.7e9 / 10e-3 / 1e9) < 0.01
+    assert r["floors_ms"]["hbm"] > r["floors_ms"]["compute"]
+    assert abs(r["tflops"] - alg["wgrad"] / 10e-3 / 1e12) < 0.01
+    # mid forward GEMM: 1.134 TFLOP (0.45 ms) against 1.77 GB (0.22 ms): MFMA binds
+    alg = {"group_gemm": 1.134e12, "group_gemm_min_bytes": 1.77e9}
+    g = bench.stage_roofline("group_gemm", alg, 1.0, {}, False)
+    assert g["bound"] == "mfma" and g["unit"] == "TFLOP/s" and g["achieved"] == g["tflops"]
+    # float32 GEMMs price against the fp32 vector peak
+    f = bench.stage_roofline("group_gemm", alg, 1.0, {}, True)
+    assert f["bound"] == "alu" and f["peak"] == bench.MFMA_F32_VECTOR_TFLOPS

@@ -5,8 +5,9 @@ swiglu and its gradient are float32 arithmetic rounded once to the row dtype: |g
 2^-8 |ref| for bf16 (one rounding plus a few float32 ulps), 1e-6 |ref| for float32, plus 1e-6 times
 the size of the gradient's terms where its factor (1 + g(1 - s)) crosses zero.  The tiny float32
 FFN layer (forward and backward) is held to 1e-4 (1 + |ref|) against the oracle's planned chain; the
-mid bf16 FFN at full size to the bf16-GEMM bound on sampled tokens, with the oracle rounding the
-intermediates to bf16 at the same points (Ygu, A, dYp).
+mid bf16 FFN at full size to the bf16-GEMM bound on sampled tokens and on the whole weight gradients
+of three experts (two with slot copies), with the oracle rounding the intermediates to bf16 at the same
+points (Ygu, A, dYp, dA, dYgu).
 """
 import numpy as np
 import pytest
@@ -150,7 +151,7 @@ def test_tiny_ffn_layer_forward_backward(m):
     assert float(L.dW_gu_slots.abs().max()) == 0.0 and float(L.dW_down_slots.abs().max()) == 0.0
 
 
-def test_mid_ffn_full_size_sampled(m):
+def test_mid_ffn_full_size(m):
     wl = WORKLOADS["mid_fwd"]
     R, E, B, S, K, H, Hp = wl.R, wl.E, wl.B, wl.S, wl.K, wl.H, wl.Hp
     idx, gates = router_output(R, S, E, K, 0, alpha=alpha_for(wl, 0, 1.0))
@@ -198,4 +199,28 @@ def test_mid_ffn_full_size_sampled(m):
             scale_dx += np.abs(term)
         assert np.all(np.abs(out[t] - ref_out) <= 1e-2 * (1 + scale_out)), t
         assert np.all(np.abs(dX[t] - ref_dx) <= 2e-2 * (1 + scale_dx)), t
-    assert torch.isfinite(L.dW_gu_home).all() and torch.isfinite(L.dW_down_home).all()
+    # both projections' weight gradients after wgrad + reduce_grad: the whole gradient of three experts
+    # (the two with the most slot copies and one without), from the same bf16 intermediates
+    p = oplanner.plan(idx, E, B)
+    copies = np.bincount(p.slot_expert[p.slot_expert >= 0], minlength=E)
+    by_copies = [int(e) for e in np.argsort(-copies, kind="stable") if copies[e] > 0]
+    experts = list(dict.fromkeys(by_copies[:2] + [int(np.nonzero(copies == 0)[0][0])]))
+    assert copies[experts[0]] > 0
+    flat_ids = np.asarray(idx).reshape(-1)
+    g32 = np.asarray(gates, dtype=np.float32).reshape(-1)
+    do32 = dout.numpy().reshape(-1, H)
+    for e in experts:
+        say("  FFN weight gradients of expert", e, "copies", int(copies[e]))
+        q = np.nonzero(flat_ids == e)[0]
+        x = X[q // K]
+        wgu, wd = Wgu[e].astype(np.float64), Wd[e].astype(np.float64)
+        ygu = bf16_round_np(x @ wgu)
+        a = bf16_round_np(olayer.swiglu(ygu))
+        dz = bf16_round_np((g32[q][:, None] * do32[q // K]).astype(np.float64))  # float32 product, rounded once
+        da = bf16_round_np(dz @ wd.T)
+        dygu = bf16_round_np(olayer.swiglu_backward(ygu, da))
+        ref_d, ref_gu = a.T @ dz, x.T @ dygu
+        got_d, got_gu = np64(L.dW_down_home[e]), np64(L.dW_gu_home[e])
+        assert np.all(np.abs(got_d - ref_d) <= 2e-2 * (1 + np.abs(a).T @ np.abs(dz))), f"dW_down[{e}]"
+        assert np.all(np.abs(got_gu - ref_gu) <= 2e-2 * (1 + np.abs(x).T @ np.abs(dygu))), f"dW_gate_up[{e}]"
+    assert float(L.dW_gu_slots.abs().max()) == 0.0 and float(L.dW_down_slots.abs().max()) == 0.0

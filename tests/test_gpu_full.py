@@ -1,11 +1,13 @@
 """Parity at the workloads' full sizes, in the launch configuration the benchmark times (GPU).
 
-The planner is compared bit for bit on every array.  Row movement and float
-results are checked on sampled outputs the oracle computes one by one from the
-generated inputs: dispatched rows bitwise, prefetched slots bitwise, GEMM rows
-within 1e-2*(1+|ref|), combined tokens and weight-gradient entries within the
-bf16-GEMM bound.  Also: bitwise run-to-run determinism, HIP-graph replay, and no
-allocation across a maxvio sweep.
+The planner is compared bit for bit on every array, at every sweep point.  Every dispatched row and
+every prefetched slot is compared bitwise.  Float results are compared element by element against the
+oracle on whole units -- every GEMM row of two whole ranks (one holding the most slot groups, and the
+last rank, whose tail holds the GEMM's last raster band), every combined token of one rank, the whole
+gradient of four experts after wgrad + reduce_grad -- within 1e-2*(1+|ref|) for the bf16 GEMMs and
+1e-2*(1+sum|g*y|) for tokens combined from bf16 rows; and every GEMM row, combined token and expert
+gradient through row-sum properties that follow from that bound.  Also: guard regions around every
+output buffer, bitwise run-to-run determinism, HIP-graph replay, and no allocation across a sweep.
 """
 import numpy as np
 import pytest
@@ -16,7 +18,8 @@ from oracle import planner as oplanner
 from synthetic import WORKLOADS
 from synthetic.calibrate import alpha_for
 from synthetic.router import TAG_DY, TAG_W, TAG_X, normal_tensor, router_output
-from tests.gpu_util import assert_gemm_close, np64, npi, say
+from tests.gpu_util import (DEV, DeviceExperts, DeviceRows, DispatchedRows, Guarded, OracleSlots,
+                            assert_gemm_close, np64, npi, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -34,10 +37,10 @@ def routing(wl, target, seed=0):
     return router_output(wl.R, wl.S, wl.E, wl.K, seed, alpha=alpha, zipf_s=wl.zipf_s)
 
 
-def build_layer(m, wl, target, backward=False, seed=0):
+def build_layer(m, wl, target, backward=False, seed=0, data_grad=False):
     idx, gates = routing(wl, target, seed)
     dt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
-    L = m.MoeLayer(wl.R, wl.E, wl.B, wl.S, wl.K, wl.H, wl.Hp, dtype=dt, backward=backward)
+    L = m.MoeLayer(wl.R, wl.E, wl.B, wl.S, wl.K, wl.H, wl.Hp, dtype=dt, backward=backward, data_grad=data_grad)
     L.topk_idx.copy_(torch.as_tensor(idx))
     L.gates.copy_(torch.as_tensor(gates))
     L.X.copy_(normal_tensor((wl.R, wl.S, wl.H), 1.0, wl.dtype, seed, TAG_X, "cuda", slices=wl.R))
@@ -48,8 +51,8 @@ def build_layer(m, wl, target, backward=False, seed=0):
     return L, idx, gates
 
 
-PLAN_CASES = [("mid_fwd", 0.0), ("mid_fwd", 1.0), ("mid_fwd", 3.0), ("large_fwd", 0.5), ("large_fwd", 4.0),
-              ("mid_bwd", 2.0), ("plan_stress", None), ("tiny_f32", None)]
+PLAN_CASES = [("mid_fwd", 0.0), ("mid_fwd", 1.0), ("mid_fwd", 3.0), ("large_fwd", 0.5), ("large_fwd", 1.0),
+              ("large_fwd", 2.0), ("large_fwd", 4.0), ("mid_bwd", 2.0), ("plan_stress", None), ("tiny_f32", None)]
 
 
 @pytest.mark.parametrize("name,target", PLAN_CASES)
@@ -81,27 +84,50 @@ def test_full_plan_bit_exact(m, name, target):
         assert abs(p.maxvio - target) < 0.06
 
 
-def _sample_rows(rng, p, wl, n_groups=6, per_group=6):
-    """Rows from a few non-empty groups, slot groups first, plus rows at group edges."""
-    rows = []
-    cands = []
-    for r in range(wl.R):
-        for g in range(wl.E + wl.B):
-            a, b = p.cu_seqlens[r, g], p.cu_seqlens[r, g + 1]
-            if b > a:
-                cands.append((g >= wl.E, r, g, a, b))
-    cands.sort(key=lambda c: not c[0])
-    pick = cands[:n_groups // 2] + [cands[i] for i in rng.choice(len(cands), n_groups - n_groups // 2,
-                                                                  replace=False)]
-    for _, r, g, a, b in pick:
-        local = {a, b - 1} | set(rng.integers(a, b, size=per_group).tolist())
-        rows += [r * wl.P + x for x in sorted(local)]
-    return np.array(sorted(set(rows)), dtype=np.int64)
+def check_ranks(p, wl):
+    """Whole ranks the float checks cover: the rank holding the most slot groups (its buffer mixes home,
+    slot and short groups) and the last rank, whose last groups hold the GEMM's last raster band."""
+    r_slots = int(np.argmax((p.slot_expert >= 0).sum(axis=1))) if wl.B > 0 else 0
+    return sorted({r_slots, wl.R - 1})
 
 
-@pytest.mark.parametrize("name,target", [("mid_fwd", 1.0), ("mid_fwd", 3.0), ("large_fwd", 4.0),
-                                         ("large_fwd", 0.5)])
-def test_full_forward_sampled(m, name, target):
+def expert_row_sums(W_home: torch.Tensor):
+    """sum_n W[e, h, n] and sum_n |W[e, h, n]| in float64 for every expert (generated weights)."""
+    ws = torch.empty(W_home.shape[:2], dtype=torch.float64, device=W_home.device)
+    wa = torch.empty_like(ws)
+    for e in range(W_home.shape[0]):
+        w = W_home[e].double()
+        ws[e] = w.sum(dim=1)
+        wa[e] = w.abs().sum(dim=1)
+    return ws, wa
+
+
+def check_projected_rows(got_rows: torch.Tensor, xrows: torch.Tensor, experts: torch.Tensor, wsum, wabs, what):
+    """Every output row at once, through the row-sum property: sum_n y[i, n] = x_i . wsum[e_i].  From the
+    element bound |y - ref| <= 1e-2 (1 + |ref|) and |ref_n| <= sum_h |x_h w_hn|, the row sums may differ by
+    at most 1e-2 (D + |x_i| . wabs[e_i])."""
+    n = got_rows.shape[0]
+    bad = 0
+    for a in range(0, n, 16384):
+        b = min(n, a + 16384)
+        x = xrows[a:b].double()
+        e = experts[a:b]
+        ref = (x * wsum[e]).sum(dim=1)
+        bound = 1e-2 * (got_rows.shape[1] + (x.abs() * wabs[e]).sum(dim=1))
+        err = (got_rows[a:b].double().sum(dim=1) - ref).abs()
+        bad += int((err > bound).sum().item())
+    assert bad == 0, f"{what}: {bad} of {n} rows break the row-sum bound"
+
+
+FWD_CASES = [("mid_fwd", 1.0), ("mid_fwd", 3.0), ("large_fwd", 0.5), ("large_fwd", 1.0), ("large_fwd", 2.0),
+             ("large_fwd", 4.0)]
+
+
+@pytest.mark.parametrize("name,target", FWD_CASES)
+def test_full_forward(m, name, target):
+    """Plan, every dispatched row (bitwise), every used slot (bitwise), every GEMM row of two whole ranks and
+    every combined token of one rank (element by element against float64), and every GEMM row and combined
+    token through the row-sum property."""
     wl = WORKLOADS[name]
     L, idx, gates = build_layer(m, wl, target)
     say("full forward", name, target)
@@ -109,46 +135,65 @@ def test_full_forward_sampled(m, name, target):
     torch.cuda.synchronize()
     p = oplanner.plan(idx, wl.E, wl.B)
     assert np.array_equal(npi(L.dest_idx), p.dest_idx)
-    rng = np.random.default_rng(0)
-    K = wl.K
-    # dispatch: sampled rows, bitwise
-    rows = rng.integers(0, wl.N, size=512)
-    Xf = L.X.reshape(-1, wl.H)
-    src_tok = torch.as_tensor(p.src_of_row[rows] // K).cuda()
-    assert torch.equal(L.Xp[torch.as_tensor(rows).cuda()], Xf[src_tok])
-    # prefetch: every used slot, bitwise
-    for r in range(wl.R):
+    assert np.array_equal(npi(L.cu_seqlens), p.cu_seqlens)
+    assert np.array_equal(npi(L.slot_expert), p.slot_expert)
+    R, S, K, H, Hp, P = wl.R, wl.S, wl.K, wl.H, wl.Hp, wl.P
+    Xf = L.X.reshape(-1, H)
+    src_tok = torch.as_tensor(p.src_of_row // K, device=DEV)
+    assert torch.equal(L.Xp, Xf[src_tok]), "dispatch: some row differs"
+    for r in range(R):
         for j in range(wl.B):
             e = p.slot_expert[r, j]
             if e >= 0:
                 assert torch.equal(L.W_slots[r, j], L.W_home[e])
-    # group GEMM: sampled rows against float64 from the generated X and W
-    rows = _sample_rows(rng, p, wl)
-    ranks, groups = olayer.row_group(p.cu_seqlens, wl.P, rows)
-    experts = {int(g if g < wl.E else p.slot_expert[r, g - wl.E]) for r, g in zip(ranks, groups)}
-    Wh = {e: np64(L.W_home[e]) for e in experts}
-    x = np64(Xf[torch.as_tensor(p.src_of_row[rows] // K).cuda()])
-    ref = np.stack([x[i] @ Wh[int(g if g < wl.E else p.slot_expert[r, g - wl.E])]
-                    for i, (r, g) in enumerate(zip(ranks, groups))])
-    assert_gemm_close(np64(L.Yp[torch.as_tensor(rows).cuda()]), ref, 1e-2, "group GEMM rows")
-    # combine: sampled tokens against the plain MoE definition
-    toks = rng.choice(wl.R * wl.S, size=12, replace=False)
-    ids = idx.reshape(-1, K)[toks]
-    g = gates.reshape(-1, K)[toks].astype(np.float64)
-    xt = np64(Xf[torch.as_tensor(toks).cuda()])
-    need = sorted(set(ids.reshape(-1).tolist()) - set(Wh))
-    Wh.update({e: np64(L.W_home[e]) for e in need})
-    ref = np.stack([sum(g[i, k] * (xt[i] @ Wh[int(ids[i, k])]) for k in range(K)) for i in range(len(toks))])
-    scale = np.stack([sum(abs(g[i, k]) * np.abs(xt[i] @ Wh[int(ids[i, k])]) for k in range(K))
-                      for i in range(len(toks))])
-    got = np64(L.out.reshape(-1, wl.Hp)[torch.as_tensor(toks).cuda()])
-    assert np.all(np.abs(got - ref) <= 1e-2 * (1 + scale)), "combined tokens"
+    W = DeviceExperts(L.W_home)
+    Ws = OracleSlots(W, p.slot_expert)
+    Xp = DispatchedRows(Xf, p.src_of_row, K)
+    ranks = check_ranks(p, wl)
+    for r in ranks:
+        say("  whole-rank GEMM rows", r)
+        ref = olayer.group_gemm(Xp, W, Ws, p.cu_seqlens, P, ranks=[r])
+        assert_gemm_close(np64(L.Yp[r * P:(r + 1) * P]), ref, 1e-2, f"group GEMM rows of rank {r}")
+    rc = ranks[0]
+    say("  combine of every token of rank", rc)
+    ids = idx.reshape(-1, K)[rc * S:(rc + 1) * S]
+    ref, scale = olayer.moe_forward_rows(np64(Xf[rc * S:(rc + 1) * S]), W, ids,
+                                         gates.reshape(-1, K)[rc * S:(rc + 1) * S])
+    got = np64(L.out.reshape(-1, Hp)[rc * S:(rc + 1) * S])
+    bad = np.abs(got - ref) > 1e-2 * (1 + scale)
+    assert not bad.any(), f"combined tokens of rank {rc}: {bad.sum()} elements outside the bound"
+    say("  row-sum property of every GEMM row and combined token")
+    wsum, wabs = expert_row_sums(L.W_home)
+    expert_of_row = torch.as_tensor(idx.reshape(-1)[p.src_of_row], device=DEV)
+    check_projected_rows(L.Yp, Xf[src_tok], expert_of_row, wsum, wabs, "group GEMM")
+    del src_tok
+    out_f = L.out.reshape(-1, Hp).double().sum(dim=1)
+    ids_t = torch.as_tensor(idx.reshape(-1, K), device=DEV).long()
+    g_t = torch.as_tensor(gates.reshape(-1, K), device=DEV).double()
+    ref_t = torch.zeros(R * S, dtype=torch.float64, device=DEV)
+    bound_t = torch.full((R * S,), 1e-2 * Hp, dtype=torch.float64, device=DEV)
+    for a in range(0, R * S, 8192):
+        b = min(R * S, a + 8192)
+        x = Xf[a:b].double()
+        for k in range(K):
+            e = ids_t[a:b, k]
+            ref_t[a:b] += g_t[a:b, k] * (x * wsum[e]).sum(dim=1)
+            bound_t[a:b] += 1e-2 * g_t[a:b, k].abs() * (x.abs() * wabs[e]).sum(dim=1)
+    nbad = int(((out_f - ref_t).abs() > bound_t).sum().item())
+    assert nbad == 0, f"combine: {nbad} tokens break the row-sum bound"
 
 
-def test_full_backward_sampled(m):
-    wl = WORKLOADS["mid_bwd"]
-    L, idx, _ = build_layer(m, wl, 2.0, backward=True)
-    say("full backward mid_bwd")
+BWD_CASES = [("mid_bwd", 2.0), ("large_fwd", 1.0)]
+
+
+@pytest.mark.parametrize("name,target", BWD_CASES)
+def test_full_weight_gradient(m, name, target):
+    """wgrad + reduce_grad at full size: the whole [H, H'] gradient of four experts (the two with the most
+    slot copies, the hottest, and one without copies) element by element against float64, every expert's
+    row and column sums through the same property, and every slot cleared."""
+    wl = WORKLOADS[name]
+    L, idx, _ = build_layer(m, wl, target, backward=True)
+    say("full weight gradient", name, target)
     L.plan()
     L.dispatch()
     L.wgrad()
@@ -158,35 +203,129 @@ def test_full_backward_sampled(m):
     assert np.array_equal(npi(L.dest_idx), p.dest_idx)
     assert p.stats[1] > 0
     assert float(L.dW_slots.abs().max().item()) == 0.0  # every slot consumed and cleared
-    rng = np.random.default_rng(1)
-    ids = idx.reshape(-1)
-    with_copies = sorted(set(p.slot_expert[p.slot_expert >= 0].tolist()))
-    experts = with_copies[:3] + [int(e) for e in rng.choice(wl.E, 3, replace=False)]
-    Xf = L.X.reshape(-1, wl.H)
-    for e in experts:
-        q = np.nonzero(ids == e)[0]
-        hs = rng.integers(0, wl.H, size=8)
-        ns = rng.integers(0, wl.Hp, size=8)
-        xcols = np64(Xf[torch.as_tensor(q // wl.K).cuda()][:, torch.as_tensor(hs).cuda()])  # [n_e, 8]
-        dyrows = np64(L.dY[torch.as_tensor(p.dest_idx.reshape(-1)[q]).cuda()][:, torch.as_tensor(ns).cuda()])
-        ref = xcols.T @ dyrows  # [8, 8]
-        got = np64(L.dW_home[e][torch.as_tensor(hs).cuda()][:, torch.as_tensor(ns).cuda()])
-        assert_gemm_close(got, ref, 1e-2, f"dW_home[{e}]")
+    R, S, K, H, Hp = wl.R, wl.S, wl.K, wl.H, wl.Hp
+    copies = np.bincount(p.slot_expert[p.slot_expert >= 0], minlength=wl.E)
+    by_copies = [int(e) for e in np.argsort(-copies, kind="stable") if copies[e] > 0]
+    hottest = int(np.argmax(p.expert_counts))
+    lone = int(np.nonzero(copies == 0)[0][0])
+    experts = list(dict.fromkeys(by_copies[:2] + [hottest, lone]))
+    X = L.X.float().cpu().numpy()  # bf16 values, exact in float32
+    dY_of_pair = DeviceRows(L.dY, index=p.dest_idx.reshape(-1))  # the gradient row of each pair
+    ref = olayer.expert_weight_grad(X, dY_of_pair, idx, wl.E, experts=experts)
+    for i, e in enumerate(experts):
+        say("  dW_home of expert", e, "copies", int(copies[e]))
+        assert_gemm_close(np64(L.dW_home[e]), ref[i], 1e-2, f"dW_home[{e}]")
+    say("  row and column sums of every expert's gradient")
+    Xf = L.X.reshape(-1, H)
+    dest = torch.as_tensor(p.dest_idx.reshape(-1), device=DEV).long()
+    ids = torch.as_tensor(idx.reshape(-1), device=DEV).long()
+    for e in range(wl.E):
+        q = torch.nonzero(ids == e).flatten()
+        if q.numel() == 0:
+            assert float(L.dW_home[e].abs().max().item()) == 0.0
+            continue
+        x = Xf[q // K].double()
+        dy = L.dY[dest[q]].double()
+        dw = L.dW_home[e].double()
+        col_ref = x.sum(dim=1) @ dy  # sum_h dW[h, n] = sum_i (sum_h x_ih) dy_in
+        col_bound = 1e-2 * (H + x.abs().sum(dim=1) @ dy.abs())
+        row_ref = x.T @ dy.sum(dim=1)  # sum_n dW[h, n]
+        row_bound = 1e-2 * (Hp + x.abs().T @ dy.abs().sum(dim=1))
+        assert bool(((dw.sum(dim=0) - col_ref).abs() <= col_bound).all()), f"column sums of dW_home[{e}]"
+        assert bool(((dw.sum(dim=1) - row_ref).abs() <= row_bound).all()), f"row sums of dW_home[{e}]"
 
 
-def test_full_stress_dispatch_sampled(m):
-    wl = WORKLOADS["plan_stress"]
-    L, idx, _ = build_layer(m, wl, None)
-    say("full stress plan+dispatch")
-    L.forward()
+@pytest.mark.parametrize("name,target", [("mid_fwd", 1.0), ("large_fwd", 1.0)])
+def test_full_dgrad_and_dispatch_backward(m, name, target):
+    """dgrad on a generated dYp (the dY buffer, seeded N(0,1)): every dXp row of two whole ranks element by
+    element against float64 and every row through the row-sum property; then dispatch backward: every
+    token of one rank against the plain input gradient, its rows being sums of K bf16-rounded dXp rows."""
+    wl = WORKLOADS[name]
+    L, idx, _ = build_layer(m, wl, target, backward=True, data_grad=True)
+    L.dY.copy_(normal_tensor((wl.N, wl.Hp), 1.0, wl.dtype, 0, TAG_DY, "cuda", slices=wl.R))
+    say("full dgrad + dispatch backward", name, target)
+    L.plan()
+    L.prefetch()
+    L.dgrad()
+    L.dispatch_backward()
     torch.cuda.synchronize()
     p = oplanner.plan(idx, wl.E, wl.B)
     assert np.array_equal(npi(L.dest_idx), p.dest_idx)
+    R, S, K, H, Hp, P = wl.R, wl.S, wl.K, wl.H, wl.Hp, wl.P
+    W = DeviceExperts(L.W_home)
+    Ws = OracleSlots(W, p.slot_expert)
+    dY = DeviceRows(L.dY)
+    ranks = check_ranks(p, wl)
+    for r in ranks:
+        say("  whole-rank dXp rows", r)
+        ref = olayer.group_gemm_dgrad(dY, W, Ws, p.cu_seqlens, P, ranks=[r])
+        assert_gemm_close(np64(L.dXp[r * P:(r + 1) * P]), ref, 1e-2, f"dXp rows of rank {r}")
+    rc = ranks[0]
+    say("  dX of every token of rank", rc)
+    dest_rc = p.dest_idx[rc]  # [S, K]
+    dY_rows = np64(L.dY[torch.as_tensor(dest_rc.reshape(-1), device=DEV)]).reshape(S, K, Hp)
+    ref, scale = olayer.moe_input_grad_rows(dY_rows, W, idx[rc])
+    got = np64(L.dX[rc])
+    bad = np.abs(got - ref) > 1e-2 * (K + scale)
+    assert not bad.any(), f"dX of rank {rc}: {bad.sum()} elements outside the bound"
+    say("  row-sum property of every dXp row")
+    csum = torch.empty((wl.E, Hp), dtype=torch.float64, device=DEV)
+    cabs = torch.empty_like(csum)
+    for e in range(wl.E):
+        w = L.W_home[e].double()
+        csum[e] = w.sum(dim=0)
+        cabs[e] = w.abs().sum(dim=0)
+    expert_of_row = torch.as_tensor(idx.reshape(-1)[p.src_of_row], device=DEV)
+    check_projected_rows(L.dXp, L.dY, expert_of_row, csum, cabs, "dgrad")
+
+
+def test_guard_regions_around_every_output(m):
+    """Every stage of the forward, the weight backward and the data backward at the large workload's most
+    skewed point, with each output inside a guarded allocation: after each stage, nothing has been written
+    outside any output buffer."""
+    wl = WORKLOADS["large_fwd"]
+    L, _, _ = build_layer(m, wl, 4.0, backward=True, data_grad=True)
+    L.dout.normal_(generator=torch.Generator(device="cuda").manual_seed(3))
+    guards = {}
+    for name in ("expert_counts", "cu_seqlens", "slot_expert", "dest_idx", "src_of_row", "stats", "Xp", "W_slots",
+                 "Yp", "out", "dW_home", "dW_slots", "dY", "dgates", "dXp", "dX"):
+        t = getattr(L, name)
+        g = Guarded(t.shape, t.dtype)
+        g.view.copy_(t)
+        setattr(L, name, g.view)
+        guards[name] = g
+    torch.cuda.synchronize()
+    stages = [("plan", L.plan), ("prefetch", L.prefetch), ("dispatch", L.dispatch), ("group_gemm", L.group_gemm),
+              ("combine", L.combine), ("combine_backward", L.combine_backward), ("wgrad", L.wgrad),
+              ("reduce_grad", L.reduce_grad), ("dgrad", L.dgrad), ("dispatch_backward", L.dispatch_backward)]
+    for name, f in stages:
+        say("  guarded stage", name)
+        f()
+        torch.cuda.synchronize()
+        broken = [n for n, g in guards.items() if not g.intact()]
+        assert not broken, f"{name} wrote outside {broken}"
+    assert int(L.stats[1].item()) > 0
+
+
+def test_full_stress_dispatch(m):
+    """The routing-stress workload (1 048 576 pairs, maxvio ~ 46, direct reads): every dispatched row
+    bitwise, with the dispatched buffer inside a guarded allocation."""
+    wl = WORKLOADS["plan_stress"]
+    L, idx, _ = build_layer(m, wl, None)
+    g = Guarded(L.Xp.shape, L.Xp.dtype)
+    L.Xp = g.view
+    say("full stress plan+dispatch")
+    L.forward()
+    torch.cuda.synchronize()
+    assert g.intact()
+    p = oplanner.plan(idx, wl.E, wl.B)
+    assert np.array_equal(npi(L.dest_idx), p.dest_idx)
     assert p.stats[2] > 0  # inference budget B=4: direct reads happen
-    rng = np.random.default_rng(2)
-    rows = rng.integers(0, wl.N, size=2048)
-    src_tok = torch.as_tensor(p.src_of_row[rows] // wl.K).cuda()
-    assert torch.equal(L.Xp[torch.as_tensor(rows).cuda()], L.X.reshape(-1, wl.H)[src_tok])
+    Xf = L.X.reshape(-1, wl.H)
+    for a in range(0, wl.N, 1 << 18):  # every row, a quarter million at a time
+        b = min(wl.N, a + (1 << 18))
+        src_tok = torch.as_tensor(p.src_of_row[a:b] // wl.K, device=DEV)
+        assert torch.equal(L.Xp[a:b], Xf[src_tok]), f"dispatched rows [{a}, {b})"
 
 
 def test_run_to_run_bitwise(m):

@@ -189,3 +189,42 @@ def test_pins_catch_dropped_slot_gradient(monkeypatch):
         assert not np.allclose(dWh, ref)
         return
     pytest.fail("no case with a slot")
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_block_forms_equal_the_plain_definitions(seed):
+    # the whole-rank, token-block and expert-subset forms that the full-size GPU checks use give the same
+    # numbers as the pinned plain forms (H = 8 != H' = 6, so a missing transpose cannot even run)
+    c = _case(seed)
+    R, S, K, H, Hp, E = c["R"], c["S"], c["K"], c["H"], c["Hp"], c["E"]
+    P = S * K
+    rng = c["rng"]
+    p, Xp, Ws, Yp, _ = _chain(c)
+    ranks = sorted({R - 1, 0}, reverse=True)
+    got = layer.group_gemm(Xp, c["W"], Ws, p.cu_seqlens, P, ranks=ranks)
+    assert np.array_equal(got, np.concatenate([Yp[r * P:(r + 1) * P] for r in ranks]))
+    dYp = rng.standard_normal((R * P, Hp))
+    full = layer.group_gemm_dgrad(dYp, c["W"], Ws, p.cu_seqlens, P)
+    got = layer.group_gemm_dgrad(dYp, c["W"], Ws, p.cu_seqlens, P, ranks=ranks)
+    assert np.array_equal(got, np.concatenate([full[r * P:(r + 1) * P] for r in ranks]))
+
+    toks = np.arange(R * S)[::2]
+    ids = c["idx"].reshape(-1, K)[toks]
+    g = c["gates"].reshape(-1, K)[toks]
+    out, scale = layer.moe_forward_rows(c["X"].reshape(-1, H)[toks], c["W"], ids, g)
+    ref = layer.moe_forward(c["X"], c["W"], c["idx"], c["gates"], tokens=toks)
+    assert np.allclose(out, ref, rtol=1e-13, atol=1e-13)
+    assert np.all(scale + 1e-12 >= np.abs(out))
+
+    dout = rng.standard_normal((R, S, Hp))
+    dX_ref, _ = layer.moe_backward(c["X"], c["W"], c["idx"], c["gates"], dout)
+    dY_rows = g[:, :, None] * dout.reshape(-1, Hp)[toks][:, None, :]  # gate * dout: combine's backward
+    dx, dscale = layer.moe_input_grad_rows(dY_rows, c["W"], ids)
+    assert np.allclose(dx, dX_ref.reshape(-1, H)[toks], rtol=1e-12, atol=1e-12)
+    assert np.all(dscale + 1e-12 >= np.abs(dx))
+
+    dY_of_pair = rng.standard_normal((R * S * K, Hp))
+    full = layer.expert_weight_grad(c["X"], dY_of_pair, c["idx"], E)
+    ex = sorted({E - 1, 0}, reverse=True)
+    got = layer.expert_weight_grad(c["X"], dY_of_pair, c["idx"], E, experts=ex)
+    assert np.array_equal(got, full[ex])

@@ -194,3 +194,156 @@ def test_pins_catch_unbalanced_rank(monkeypatch):
     p = planner.plan(idx, E, B)
     with pytest.raises(AssertionError):
         check_plan_invariants(idx, E, B, p.cu_seqlens, p.slot_expert, p.dest_idx)
+
+
+# ------------------------------------------------------------ the fewest-copies planner
+
+
+def _check_mincopy_example(g):
+    p = planner.plan(np.array(g["topk_idx"]), g["E"], g["B"], planner="mincopy")
+    assert p.expert_counts.tolist() == g["expert_counts"]
+    assert abs(p.maxvio - g["maxvio_num"] / g["maxvio_den"]) < 1e-15
+    assert p.keep.tolist() == g["keep"]
+    assert p.cu_seqlens.tolist() == g["cu_seqlens"]
+    assert p.slot_expert.tolist() == g["slot_expert"]
+    assert p.dest_idx.tolist() == g["dest_idx"]
+    assert p.stats.tolist() == g["stats"]
+    return p
+
+
+@pytest.mark.parametrize("name", ["plan_example1_mincopy.json", "plan_example2_mincopy.json",
+                                  "plan_example4_tie.json"])
+def test_mincopy_hand_worked_examples(name):
+    g = load(name)
+    p = _check_mincopy_example(g)
+    check_plan_invariants(g["topk_idx"], g["E"], g["B"], p.cu_seqlens, p.slot_expert, p.dest_idx, p.src_of_row,
+                          p.stats, planner="mincopy")
+    assert mincopies.min_copies(p.expert_counts, g["R"], g["S"] * g["K"]) == g["min_copies"] == p.stats[0]
+    if "prefix_keep" in g:
+        assert planner.plan(np.array(g["topk_idx"]), g["E"], g["B"]).keep.tolist() == g["prefix_keep"]
+
+
+def test_mincopy_example3_reaches_the_minimum():
+    g = load("plan_example3_counts.json")
+    idx = routing_from_counts(g["expert_counts"], g["R"], g["S"], g["K"])
+    p = planner.plan(idx, g["E"], g["B"], planner="mincopy")
+    assert [e for e in range(g["E"]) if p.over[e] > 0] == g["mincopy"]["overflow_experts"]
+    assert p.slot_expert[3].tolist() == g["mincopy"]["slot_expert_rank3"]
+    assert p.stats.tolist() == g["mincopy"]["stats"]
+    assert p.stats[0] == g["min_copies"]
+    check_plan_invariants(idx, g["E"], g["B"], p.cu_seqlens, p.slot_expert, p.dest_idx, p.src_of_row, p.stats,
+                          planner="mincopy")
+
+
+@pytest.mark.parametrize("seed", range(100))
+def test_mincopy_invariants_and_list_simulation(seed):
+    idx, E, B = _small_case(seed)
+    p = planner.plan(idx, E, B, planner="mincopy")
+    check_plan_invariants(idx, E, B, p.cu_seqlens, p.slot_expert, p.dest_idx, p.src_of_row, p.stats,
+                          planner="mincopy")
+    cu, slots, dest = list_plan(idx, E, B, planner="mincopy")
+    assert np.array_equal(cu, p.cu_seqlens)
+    assert np.array_equal(slots, p.slot_expert)
+    assert np.array_equal(dest, p.dest_idx)
+    # the overflowing experts of an overloaded rank are as few as any choice allows: no smaller set of its
+    # experts holds the excess (brute force over subsets)
+    from itertools import combinations
+    R = idx.shape[0]
+    per = E // R
+    for r in range(R):
+        T = p.expert_counts[r * per:(r + 1) * per]
+        x = int(T.sum()) - idx.shape[1] * idx.shape[2]
+        n_over = int(np.sum(p.over[r * per:(r + 1) * per] > 0))
+        if x <= 0:
+            assert n_over == 0
+            continue
+        least = min(m for m in range(1, per + 1) for c in combinations(T.tolist(), m) if sum(c) >= x)
+        assert n_over == least
+
+
+def test_mincopy_never_above_prefix_and_never_below_the_minimum():
+    for seed in range(60):
+        idx, E, B = _small_case(seed)
+        R, S, K = idx.shape
+        a = planner.plan(idx, E, B)
+        b = planner.plan(idx, E, B, planner="mincopy")
+        assert b.stats[0] <= a.stats[0]
+        if R >= 2 and E // R <= 2:
+            assert mincopies.min_copies(b.expert_counts, R, S * K) <= b.stats[0]
+
+
+def test_slot_capped_minimum():
+    # example 2 (B = 1): two copies leave one for a direct read; one copy of expert 0 fits the slot
+    g = load("plan_example2.json")
+    T = np.array(g["expert_counts"])
+    assert mincopies.min_copies(T, g["R"], g["S"] * g["K"], slot_cap=1) == 1
+    # example 3 counts (ranks 0-2 over by 2 each, rank 3 short by 6): even one slot per rank allows the
+    # minimum of 3 copies, as a chain -- expert 8 sends 2 pairs to rank 1, expert 4 sends 4 to rank 0,
+    # expert 0 sends 6 to rank 3 -- while no slots at all (cap 0) admit no balanced placement
+    g = load("plan_example3_counts.json")
+    T = np.array(g["expert_counts"])
+    P = g["S"] * g["K"]
+    assert mincopies.min_copies(T, g["R"], P, max_size=3, slot_cap=3) == 3
+    assert mincopies.min_copies(T, g["R"], P, max_size=3, slot_cap=1) == 3
+    assert mincopies.min_copies(T, g["R"], P, max_size=3, slot_cap=0) is None
+    per = g["E"] // g["R"]
+    assert mincopies._feasible(T, g["R"], P, [e // per for e in range(g["E"])], [(8, 1), (4, 0), (0, 3)])
+
+
+def test_planner_gap_report_matches_the_stored_table():
+    # the distribution quoted in the design notes: copies of both planners against the brute-force minimum
+    from tests import planner_gap
+    with open(planner_gap.GOLDEN) as f:
+        stored = json.load(f)
+    n = 60  # a prefix of the stored cases keeps the CPU suite quick; the summary covers all of them
+    for seed in range(n):
+        assert planner_gap.measure(seed) == stored["cases"][seed], seed
+    assert planner_gap.summary(stored["cases"]) == stored["summary"]
+    s = stored["summary"]
+    assert s["copies_total"]["min"] <= s["copies_total"]["mincopy"] <= s["copies_total"]["prefix"]
+    for r in stored["cases"]:
+        assert r["lower_bound"] <= r["min"] <= r["mincopy"][0] <= r["prefix"][0]
+        assert r["min_capped"] is None or r["min_capped"] >= r["min"]
+
+
+def test_pins_catch_reversed_tie_order(monkeypatch):
+    # equal counts broken toward the higher id: example 4 then overflows expert 1
+    real = planner.keep_counts
+
+    def higher_id_first(T, R, P, name="prefix"):
+        if name != "mincopy":
+            return real(T, R, P, name)
+        keep, load = real(T[::-1].copy(), R, P, name)  # mirror the expert order inside every rank
+        return keep[::-1].copy(), load[::-1].copy()
+
+    monkeypatch.setattr(planner, "keep_counts", higher_id_first)
+    with pytest.raises(AssertionError):
+        _check_mincopy_example(load("plan_example4_tie.json"))
+
+
+def test_pins_catch_smallest_first(monkeypatch):
+    def smallest_first(T, R, P, name="prefix"):
+        E = len(T)
+        per = E // R
+        keep, load = T.copy(), np.zeros(R, dtype=np.int64)
+        for r in range(R):
+            ex = list(range(r * per, (r + 1) * per))
+            load[r] = T[ex].sum()
+            x = load[r] - P
+            for e in sorted(ex, key=lambda e: (T[e], e)):
+                m = max(0, min(int(T[e]), x))
+                keep[e] -= m
+                x -= m
+        return keep, load
+
+    monkeypatch.setattr(planner, "keep_counts", smallest_first)
+    with pytest.raises(AssertionError):
+        _check_mincopy_example(load("plan_example1_mincopy.json"))
+    idx, E, B = _small_case(9)
+    p = planner.plan(idx, E, B, planner="mincopy")
+    with pytest.raises(AssertionError):
+        for seed in range(40):
+            idx, E, B = _small_case(seed)
+            p = planner.plan(idx, E, B, planner="mincopy")
+            check_plan_invariants(idx, E, B, p.cu_seqlens, p.slot_expert, p.dest_idx, p.src_of_row, p.stats,
+                                  planner="mincopy")
