@@ -833,6 +833,66 @@ def extra_workloads(args, alpha_of, no_ffn):
     return out
 
 
+PLANNER_POINTS = (("tiny_f32", (None,)), ("mid_fwd", (0.0, 1.0, 3.0)), ("large_fwd", (0.5, 1.0, 2.0, 4.0)),
+                  ("mid_bwd", (2.0,)), ("plan_stress", (None,)))
+
+
+def planner_table(args, alpha_of, reps=10):
+    """Both planners on every workload's routing: copies (slotted, direct reads), the prefetch and reduce_grad
+    bytes those copies cost (2*H*H'*b per slotted copy; 4*H*H'*(2 per expert with copies + 2 per copy)), and
+    the plan's own time (HIP events around `reps` back-to-back plans, after 2 untimed)."""
+    import numpy as np
+    import torch
+
+    import load_balanced_dispatch_amd as m
+    from synthetic import WORKLOADS
+    from synthetic.router import router_output
+    out = {}
+    for name, points in PLANNER_POINTS:
+        wl = WORKLOADS[name]
+        d = m.make_dims(wl.R, wl.E, wl.B, wl.S, wl.K)
+        dev = dict(device="cuda")
+        bufs = dict(counts=torch.empty(wl.E, dtype=torch.int32, **dev), mv=torch.empty(1, dtype=torch.float64, **dev),
+                    cu=torch.empty((wl.R, wl.E + wl.B + 1), dtype=torch.int32, **dev),
+                    slots=torch.empty((wl.R, wl.B), dtype=torch.int32, **dev) if wl.B else None,
+                    dest=torch.empty((wl.R, wl.S, wl.K), dtype=torch.int32, **dev),
+                    stats=torch.empty(4, dtype=torch.int32, **dev))
+        ws = torch.empty(m.moonep_plan_workspace_bytes(d), dtype=torch.uint8, **dev)
+        b = 4 if wl.dtype == "f32" else 2
+        rows = []
+        for tgt in points:
+            idx, _ = router_output(wl.R, wl.S, wl.E, wl.K, args.seed, alpha=alpha_of(wl, tgt), zipf_s=wl.zipf_s)
+            topk = torch.as_tensor(idx).cuda()
+            row = {"maxvio_target": tgt}
+            for planner in ("prefix", "mincopy"):
+                def run():
+                    m.moonep_plan_ex(d, planner, topk, bufs["counts"], bufs["mv"], bufs["cu"], bufs["slots"],
+                                     bufs["dest"], None, bufs["stats"], ws)
+                for _ in range(2):
+                    run()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(reps):
+                    run()
+                e1.record()
+                torch.cuda.synchronize()
+                stats = bufs["stats"].cpu().numpy()
+                slots = bufs["slots"].cpu().numpy() if wl.B else np.zeros((wl.R, 0), dtype=np.int32)
+                used = slots[slots >= 0]
+                r = {"copies_slotted_direct": stats[:3].tolist(), "plan_ms": round(e0.elapsed_time(e1) / reps, 4)}
+                if wl.Hp is not None:
+                    hh = wl.H * wl.Hp
+                    r["prefetch_bytes"] = 2 * hh * b * int(stats[1])
+                    r["reduce_grad_bytes"] = 4 * hh * (2 * len(np.unique(used)) + 2 * len(used))
+                row[planner] = r
+                row["maxvio"] = round(float(bufs["mv"].item()), 4)
+            rows.append(row)
+        out[name] = rows
+        del bufs, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -943,13 +1003,24 @@ def main():
     dominant = max(st, key=lambda n: st[n])
     roofline = dict(rooflines[dominant], stage=dominant)
     sweep, flat = sweep_summary(wl, L, results, points)
+    sweep_mincopy = None
+    if args.workload in SWEEPS and not args.no_sweep and not args.no_extras:
+        log("the same sweep with the fewest-copies planner")
+        L.planner = "mincopy"
+        res_mc = run_points(wl, L, backward, points, None, max(5, args.steps // 2), args.warmup, args.seed, alpha_of)
+        sw_mc, flat_mc = sweep_summary(wl, L, res_mc, points)
+        sweep_mincopy = {"sweep": sw_mc, "sweep_flatness": flat_mc}
+        L.planner = "prefix"
     vendor = vendor_gemm_tflops(wl) if (wl.Hp is not None and wl.dtype == "bf16") else None
     del L
     torch.cuda.empty_cache()
 
     extras = None
+    planners = None
     if args.workload == "large" and not args.no_extras:
         extras = extra_workloads(args, alpha_of, args.no_ffn)
+        log("both planners on every workload's routing")
+        planners = planner_table(args, alpha_of)
         comp["stress_plan_dispatch_pairs_per_s"] = extras["plan_stress"]["plan_dispatch_pairs_per_s"]
         comp["stress_dispatch_GBs"] = extras["plan_stress"]["dispatch"]["achieved"]
         comp["mid_plan_dispatch_pairs_per_s"] = extras["mid_fwd"]["plan_dispatch_pairs_per_s"]
@@ -1002,6 +1073,8 @@ def main():
                                     "flop rate over that."},
         "sweep": sweep,
         "sweep_flatness": flat,
+        "sweep_mincopy_planner": sweep_mincopy,
+        "planners": planners,
         "other_workloads": extras,
     }
     print(json.dumps(line), flush=True)

@@ -77,6 +77,12 @@ typedef void* moonep_stream; /* a hipStream_t */
 /* Text of the last error raised on the calling thread ("" when none). */
 const char* moonep_last_error(void);
 
+/* Planners of moonep_plan_ex. */
+typedef enum moonep_planner {
+  MOONEP_PLAN_PREFIX = 0, /* home-first prefix: each rank keeps the first S*K pairs of its home experts */
+  MOONEP_PLAN_MINCOPY = 1 /* fewest copies: an overloaded rank's excess leaves through its largest experts */
+} moonep_planner;
+
 /* Bytes of device workspace moonep_plan needs for these dims (256-byte aligned pointer). */
 size_t moonep_plan_workspace_bytes(moonep_dims d);
 
@@ -116,6 +122,22 @@ size_t moonep_plan_workspace_bytes(moonep_dims d);
 int moonep_plan(moonep_dims d, const int32_t* topk_idx, int32_t* expert_counts, double* maxvio,
                 int32_t* cu_seqlens, int32_t* slot_expert, int32_t* dest_idx, int32_t* src_of_row,
                 int32_t* stats, void* workspace, moonep_stream stream);
+
+/*
+ * moonep_plan_ex -- moonep_plan with a choice of planner (a moonep_planner value; anything else is
+ * MOONEP_EINVAL).  The pages describe their planner as one that keeps the number of redundant experts
+ * small ([P1] abstract; [P2] "Core technique: dynamic redundant experts") without printing its program.
+ * MOONEP_PLAN_PREFIX is moonep_plan.  MOONEP_PLAN_MINCOPY changes only which pairs stay home: a rank
+ * with L_r > P pairs sends its excess L_r - P out of its home experts taken largest first (equal counts:
+ * lower id first), each overflowing what is still needed, so the excess leaves through the fewest
+ * experts; every expert keeps the first keep_e pairs of its (src rank, token, k)-ordered list.  The
+ * overflow list, the contiguous cut into deficits in rank order, slots, direct reads past B, cu_seqlens
+ * and destinations then follow exactly as in moonep_plan.  Arguments, layouts, workspace (the same
+ * moonep_plan_workspace_bytes) and limits are those of moonep_plan.
+ */
+int moonep_plan_ex(moonep_dims d, int32_t planner, const int32_t* topk_idx, int32_t* expert_counts,
+                   double* maxvio, int32_t* cu_seqlens, int32_t* slot_expert, int32_t* dest_idx,
+                   int32_t* src_of_row, int32_t* stats, void* workspace, moonep_stream stream);
 
 /*
  * moonep_dispatch -- fused permute ([P2] "Core technique": each token row is

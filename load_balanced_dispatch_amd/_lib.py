@@ -18,6 +18,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoonep.so")
 
 MOONEP_F32, MOONEP_BF16 = 0, 1
+MOONEP_PLAN_PREFIX, MOONEP_PLAN_MINCOPY = 0, 1
+PLANNERS = {"prefix": MOONEP_PLAN_PREFIX, "mincopy": MOONEP_PLAN_MINCOPY}
 MOONEP_OK, MOONEP_EINVAL, MOONEP_EHIP, MOONEP_EUNSUPPORTED = 0, -1, -2, -3
 _CODES = {MOONEP_EINVAL: "EINVAL", MOONEP_EHIP: "EHIP", MOONEP_EUNSUPPORTED: "EUNSUPPORTED"}
 
@@ -57,6 +59,7 @@ def _load():
         "moonep_last_error": (ctypes.c_char_p, []),
         "moonep_plan_workspace_bytes": (sz, [Dims]),
         "moonep_plan": (ctypes.c_int, [Dims, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
+        "moonep_plan_ex": (ctypes.c_int, [Dims, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
         "moonep_dispatch": (ctypes.c_int, [Dims, i32, ctypes.c_int, vp, vp, vp, vp]),
         "moonep_prefetch": (ctypes.c_int, [Dims, i32, i32, ctypes.c_int, vp, vp, vp, vp]),
         "moonep_group_gemm_workspace_bytes": (sz, [Dims]),
@@ -81,7 +84,8 @@ def _load():
 _LIB = _load()
 
 # exported symbol names, as declared in include/moonep.h
-SYMBOLS = ("moonep_last_error", "moonep_plan_workspace_bytes", "moonep_plan", "moonep_dispatch", "moonep_prefetch",
+SYMBOLS = ("moonep_last_error", "moonep_plan_workspace_bytes", "moonep_plan", "moonep_plan_ex", "moonep_dispatch",
+           "moonep_prefetch",
            "moonep_group_gemm_workspace_bytes", "moonep_group_gemm", "moonep_combine",
            "moonep_wgrad_workspace_bytes", "moonep_wgrad", "moonep_reduce_grad", "moonep_combine_backward",
            "moonep_group_gemm_dgrad", "moonep_dispatch_backward", "moonep_swiglu", "moonep_swiglu_backward")
@@ -156,6 +160,21 @@ def moonep_wgrad_workspace_bytes(d: Dims) -> int:
 
 def moonep_plan(d: Dims, topk_idx, expert_counts, maxvio, cu_seqlens, slot_expert, dest_idx, src_of_row, stats,
                 workspace, stream=None):
+    moonep_plan_ex(d, MOONEP_PLAN_PREFIX, topk_idx, expert_counts, maxvio, cu_seqlens, slot_expert, dest_idx,
+                   src_of_row, stats, workspace, stream)
+
+
+def _planner_code(planner) -> int:
+    if isinstance(planner, str):
+        if planner not in PLANNERS:
+            raise ValueError(f"unknown planner {planner!r}; one of {sorted(PLANNERS)}")
+        return PLANNERS[planner]
+    return int(planner)
+
+
+def moonep_plan_ex(d: Dims, planner, topk_idx, expert_counts, maxvio, cu_seqlens, slot_expert, dest_idx, src_of_row,
+                   stats, workspace, stream=None):
+    """moonep_plan with a planner: "prefix" (MOONEP_PLAN_PREFIX) or "mincopy" (MOONEP_PLAN_MINCOPY)."""
     import torch
     i32 = torch.int32
     args = (
@@ -171,7 +190,7 @@ def moonep_plan(d: Dims, topk_idx, expert_counts, maxvio, cu_seqlens, slot_exper
     )
     if workspace.numel() * workspace.element_size() < moonep_plan_workspace_bytes(d):
         raise ValueError("plan workspace too small")
-    _check(_LIB.moonep_plan(d, *args, _stream(stream)))
+    _check(_LIB.moonep_plan_ex(d, _planner_code(planner), *args, _stream(stream)))
 
 
 def moonep_dispatch(d: Dims, H: int, X, dest_idx, Xp, stream=None):

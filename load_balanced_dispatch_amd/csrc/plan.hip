@@ -7,6 +7,9 @@
 //     keeps the first P pairs of its home experts' (expert, src, token, k)-ordered
 //     list; the overflow of all ranks, in ascending (expert, order), is cut
 //     contiguously into the deficits of the underloaded ranks in rank order.
+//     The fewest-copies planner differs only in the keep counts: an overloaded
+//     rank's excess leaves through its largest experts (the pages' planner keeps
+//     the number of redundant experts small; its program is not printed).
 //   * arriving experts take slots E+j (j < B), beyond that they read their home
 //     row; cu_seqlens delimits the E+B groups ([P2] "Memory contract and weight
 //     layout").
@@ -16,8 +19,10 @@
 //               pairs, invalid / repeated ids counted.
 //   plan_scan   column-wise exclusive scan of the U x E block histograms (64
 //               experts per block, 16 waves split the U rows), totals = T_e.
-//   plan_solve  one 1024-thread block: keep/overflow/deficit prefix sums,
-//               slot assignment, cu_seqlens, stats, maxvio.  O(E + R + R*(E+B)).
+//   plan_solve  one 1024-thread block: keep counts (home-first prefix, or the
+//               fewest-copies choice of overflowing experts), overflow/deficit
+//               prefix sums, slot assignment, cu_seqlens, stats, maxvio.
+//               O(E + R + R*(E+B)), plus O(E*E/R) for the fewest-copies keep.
 //   plan_emit   grid = U: stable rank of every pair inside its expert (wave
 //               ballot match + per-wave LDS counters, tiles processed in order),
 //               then its destination row.
@@ -173,7 +178,7 @@ __device__ __forceinline__ int overlap(int a0, int a1, int b0, int b1) {
 }
 
 __global__ __launch_bounds__(kSolveThreads) void plan_solve(
-    int R, int E, int B, int P, int64_t N, int U, const int32_t* __restrict__ counts,
+    int R, int E, int B, int P, int64_t N, int U, int planner, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ err, double* __restrict__ maxvio, int32_t* __restrict__ cu,
     int32_t* __restrict__ slot_expert, int32_t* __restrict__ stats, int32_t* __restrict__ g_keep,
     int32_t* __restrict__ g_ovstart, int32_t* __restrict__ g_npos, int32_t* __restrict__ g_defstart,
@@ -217,16 +222,44 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(
     stats[3] = b;
   }
 
-  // home-first keep counts per rank
-  for (int r = t; r < R; r += nt) {
-    int before = 0;
-    for (int e = r * per; e < (r + 1) * per; ++e) {
-      const int k = min(max(P - before, 0), sT[e]);
-      skeep[e] = k;
-      sover[e] = sT[e] - k;
-      before += sT[e];
+  if (planner == MOONEP_PLAN_PREFIX) {
+    // home-first keep counts: each rank keeps the first P pairs of its experts in ascending order
+    for (int r = t; r < R; r += nt) {
+      int before = 0;
+      for (int e = r * per; e < (r + 1) * per; ++e) {
+        const int k = min(max(P - before, 0), sT[e]);
+        skeep[e] = k;
+        sover[e] = sT[e] - k;
+        before += sT[e];
+      }
+      sdef[r] = max(0, P - before);
     }
-    sdef[r] = max(0, P - before);
+  } else {
+    // fewest copies: an overloaded rank's excess x leaves through its experts taken largest first
+    // (equal counts: lower id first).  Expert e overflows what x still needs after the experts ahead
+    // of it in that order, clamped to [0, T_e]; one thread per expert, O(E/R) each.
+    for (int r = t; r < R; r += nt) {
+      int load = 0;
+      for (int e = r * per; e < (r + 1) * per; ++e) load += sT[e];
+      sdef[r] = P - load;  // signed for now: minus the excess of an overloaded rank
+    }
+    __syncthreads();
+    for (int e = t; e < E; e += nt) {
+      const int r = e / per, te = sT[e], x = -sdef[r];
+      int moved = 0;
+      if (x > 0 && te > 0) {
+        int ahead = 0;
+        for (int f = r * per; f < (r + 1) * per; ++f) {
+          const int tf = sT[f];
+          ahead += (tf > te || (tf == te && f < e)) ? tf : 0;
+        }
+        moved = min(max(x - ahead, 0), te);
+      }
+      skeep[e] = te - moved;
+      sover[e] = moved;
+    }
+    __syncthreads();
+    for (int r = t; r < R; r += nt) sdef[r] = max(0, sdef[r]);
   }
   __syncthreads();
   for (int e = t; e < E; e += nt) {
@@ -443,7 +476,16 @@ extern "C" size_t moonep_plan_workspace_bytes(moonep_dims d) {
 extern "C" int moonep_plan(moonep_dims d, const int32_t* topk_idx, int32_t* expert_counts, double* maxvio,
                            int32_t* cu_seqlens, int32_t* slot_expert, int32_t* dest_idx, int32_t* src_of_row,
                            int32_t* stats, void* workspace, moonep_stream stream) {
+  return moonep_plan_ex(d, MOONEP_PLAN_PREFIX, topk_idx, expert_counts, maxvio, cu_seqlens, slot_expert, dest_idx,
+                        src_of_row, stats, workspace, stream);
+}
+
+extern "C" int moonep_plan_ex(moonep_dims d, int32_t planner, const int32_t* topk_idx, int32_t* expert_counts,
+                              double* maxvio, int32_t* cu_seqlens, int32_t* slot_expert, int32_t* dest_idx,
+                              int32_t* src_of_row, int32_t* stats, void* workspace, moonep_stream stream) {
   if (int rc = check_dims(d, "moonep_plan")) return rc;
+  MOONEP_REQUIRE(planner == MOONEP_PLAN_PREFIX || planner == MOONEP_PLAN_MINCOPY, "moonep_plan: unknown planner %d",
+                 (int)planner);
   const int64_t N = n_pairs(d);
   MOONEP_REQUIRE(d.E <= kMaxExperts, "moonep_plan: E=%d exceeds the supported %d", d.E, kMaxExperts);
   MOONEP_REQUIRE(d.R <= kMaxRanks, "moonep_plan: R=%d exceeds the supported %d", d.R, kMaxRanks);
@@ -479,7 +521,7 @@ extern "C" int moonep_plan(moonep_dims d, const int32_t* topk_idx, int32_t* expe
     if (lds > 65536)
       (void)hipFuncSetAttribute((const void*)plan_solve, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     hipLaunchKernelGGL(plan_solve, dim3(1), dim3(kSolveThreads), lds, s, d.R, d.E, d.B, P, N, geo.units,
-                       expert_counts, ws.err, maxvio, cu_seqlens, slot_expert, stats, ws.keep, ws.ovstart, ws.npos,
+                       (int)planner, expert_counts, ws.err, maxvio, cu_seqlens, slot_expert, stats, ws.keep, ws.ovstart, ws.npos,
                        ws.defstart, ws.defend, ws.efirst);
     MOONEP_LAUNCH_CHECK("moonep_plan/solve");
   }
@@ -494,3 +536,4 @@ extern "C" int moonep_plan(moonep_dims d, const int32_t* topk_idx, int32_t* expe
   }
   return MOONEP_OK;
 }
+

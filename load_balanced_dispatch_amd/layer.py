@@ -20,8 +20,9 @@ from ._lib import Dims, make_dims
 
 class MoeLayer:
     def __init__(self, R, E, B, S, K, H, Hp=None, dtype=torch.bfloat16, device="cuda", backward=False,
-                 src_of_row=True, data_grad=False):
+                 src_of_row=True, data_grad=False, planner="prefix"):
         self.d: Dims = make_dims(R, E, B, S, K)
+        self.planner = planner  # "prefix" (home-first) or "mincopy" (fewest copies)
         d = self.d
         self.H, self.Hp, self.dtype, self.device = H, Hp, dtype, device
         i32 = dict(dtype=torch.int32, device=device)
@@ -62,9 +63,9 @@ class MoeLayer:
 
     # ---------------------------------------------------------------- steps
     def plan(self, stream=None):
-        _lib.moonep_plan(self.d, self.topk_idx, self.expert_counts, self.maxvio, self.cu_seqlens,
-                         self.slot_expert if self.d.B > 0 else None, self.dest_idx, self.src_of_row, self.stats,
-                         self.ws_plan, stream)
+        _lib.moonep_plan_ex(self.d, self.planner, self.topk_idx, self.expert_counts, self.maxvio, self.cu_seqlens,
+                            self.slot_expert if self.d.B > 0 else None, self.dest_idx, self.src_of_row, self.stats,
+                            self.ws_plan, stream)
 
     def dispatch(self, stream=None):
         _lib.moonep_dispatch(self.d, self.H, self.X, self.dest_idx, self.Xp, stream)

@@ -54,6 +54,7 @@ def test_bad_dims_rejected_everywhere(dims, msg):
     null = None
     calls = [
         lambda: L.moonep_plan(d, *([null] * 10)),
+        lambda: L.moonep_plan_ex(d, 1, *([null] * 10)),
         lambda: L.moonep_dispatch(d, 8, 1, null, null, null, null),
         lambda: L.moonep_prefetch(d, 8, 8, 1, null, null, null, null),
         lambda: L.moonep_group_gemm(d, 8, 8, 1, *([null] * 7)),
@@ -82,6 +83,18 @@ def test_plan_rejects_sizes_beyond_its_lds_tables(R, E, msg):
     d = m.make_dims(R, E, 8, 1, 2)
     assert _lib.lib().moonep_plan(d, *([None] * 10)) == _lib.MOONEP_EINVAL
     assert msg in m.last_error()
+
+
+def test_plan_ex_rejects_an_unknown_planner():
+    d = m.make_dims(2, 4, 1, 3, 1)
+    L = _lib.lib()
+    assert L.moonep_plan_ex(d, 2, *([None] * 10)) == _lib.MOONEP_EINVAL
+    assert "planner" in m.last_error()
+    assert L.moonep_plan_ex(d, -1, *([None] * 10)) == _lib.MOONEP_EINVAL
+    assert L.moonep_plan_ex(d, _lib.MOONEP_PLAN_MINCOPY, *([None] * 10)) == _lib.MOONEP_EINVAL
+    assert "null" in m.last_error()  # a valid planner gets as far as the pointer checks
+    with pytest.raises(ValueError, match="planner"):
+        _lib._planner_code("optimal")
 
 
 def test_null_pointers_rejected():

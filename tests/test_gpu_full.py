@@ -55,11 +55,12 @@ PLAN_CASES = [("mid_fwd", 0.0), ("mid_fwd", 1.0), ("mid_fwd", 3.0), ("large_fwd"
               ("large_fwd", 2.0), ("large_fwd", 4.0), ("mid_bwd", 2.0), ("plan_stress", None), ("tiny_f32", None)]
 
 
+@pytest.mark.parametrize("planner", ["prefix", "mincopy"])
 @pytest.mark.parametrize("name,target", PLAN_CASES)
-def test_full_plan_bit_exact(m, name, target):
+def test_full_plan_bit_exact(m, name, target, planner):
     wl = WORKLOADS[name]
     idx, _ = routing(wl, target)
-    say("full plan", name, target)
+    say("full plan", name, target, planner)
     d = m.make_dims(wl.R, wl.E, wl.B, wl.S, wl.K)
     dev = dict(device="cuda")
     counts = torch.empty(wl.E, dtype=torch.int32, **dev)
@@ -70,9 +71,9 @@ def test_full_plan_bit_exact(m, name, target):
     src = torch.empty(wl.N, dtype=torch.int32, **dev)
     stats = torch.empty(4, dtype=torch.int32, **dev)
     ws = torch.empty(m.moonep_plan_workspace_bytes(d), dtype=torch.uint8, **dev)
-    m.moonep_plan(d, torch.as_tensor(idx).cuda(), counts, mv, cu, slots, dest, src, stats, ws)
+    m.moonep_plan_ex(d, planner, torch.as_tensor(idx).cuda(), counts, mv, cu, slots, dest, src, stats, ws)
     torch.cuda.synchronize()
-    p = oplanner.plan(idx, wl.E, wl.B)
+    p = oplanner.plan(idx, wl.E, wl.B, planner=planner)
     assert npi(counts).tolist() == p.expert_counts.tolist()
     assert mv.item() == p.maxvio
     assert np.array_equal(npi(cu), p.cu_seqlens)
@@ -119,21 +120,23 @@ def check_projected_rows(got_rows: torch.Tensor, xrows: torch.Tensor, experts: t
     assert bad == 0, f"{what}: {bad} of {n} rows break the row-sum bound"
 
 
-FWD_CASES = [("mid_fwd", 1.0), ("mid_fwd", 3.0), ("large_fwd", 0.5), ("large_fwd", 1.0), ("large_fwd", 2.0),
-             ("large_fwd", 4.0)]
+FWD_CASES = [("mid_fwd", 1.0, "prefix"), ("mid_fwd", 3.0, "prefix"), ("large_fwd", 0.5, "prefix"),
+             ("large_fwd", 1.0, "prefix"), ("large_fwd", 2.0, "prefix"), ("large_fwd", 4.0, "prefix"),
+             ("mid_fwd", 3.0, "mincopy"), ("large_fwd", 4.0, "mincopy")]
 
 
-@pytest.mark.parametrize("name,target", FWD_CASES)
-def test_full_forward(m, name, target):
+@pytest.mark.parametrize("name,target,planner", FWD_CASES)
+def test_full_forward(m, name, target, planner):
     """Plan, every dispatched row (bitwise), every used slot (bitwise), every GEMM row of two whole ranks and
     every combined token of one rank (element by element against float64), and every GEMM row and combined
     token through the row-sum property."""
     wl = WORKLOADS[name]
     L, idx, gates = build_layer(m, wl, target)
-    say("full forward", name, target)
+    L.planner = planner
+    say("full forward", name, target, planner)
     L.forward()
     torch.cuda.synchronize()
-    p = oplanner.plan(idx, wl.E, wl.B)
+    p = oplanner.plan(idx, wl.E, wl.B, planner=planner)
     assert np.array_equal(npi(L.dest_idx), p.dest_idx)
     assert np.array_equal(npi(L.cu_seqlens), p.cu_seqlens)
     assert np.array_equal(npi(L.slot_expert), p.slot_expert)

@@ -30,7 +30,7 @@ def m():
     return mod
 
 
-def gpu_plan(m, topk, E, B, src=True):
+def gpu_plan(m, topk, E, B, src=True, planner="prefix"):
     topk = np.asarray(topk)
     R, S, K = topk.shape
     d = m.make_dims(R, E, B, S, K)
@@ -44,8 +44,8 @@ def gpu_plan(m, topk, E, B, src=True):
         stats=torch.full((4,), -7, dtype=torch.int32, device=DEV),
     )
     ws = torch.full((max(1, m.moonep_plan_workspace_bytes(d)),), 0xAB, dtype=torch.uint8, device=DEV)
-    m.moonep_plan(d, i32(topk), out["counts"], out["maxvio"], out["cu"], out["slots"], out["dest"], out["src"],
-                  out["stats"], ws)
+    m.moonep_plan_ex(d, planner, i32(topk), out["counts"], out["maxvio"], out["cu"], out["slots"], out["dest"],
+                     out["src"], out["stats"], ws)
     torch.cuda.synchronize()
     return d, out
 
@@ -118,6 +118,55 @@ def test_plan_shapes_bit_exact(m, R, E, B, S, K):
     say("plan shape", R, E, B, S, K)
     _, out = gpu_plan(m, topk, E, B)
     assert_plan_equal(out, oplanner.plan(topk, E, B), B)
+
+
+@pytest.mark.parametrize("name", ["plan_example1_mincopy.json", "plan_example2_mincopy.json",
+                                  "plan_example4_tie.json"])
+def test_plan_mincopy_hand_worked_examples(m, name):
+    g = json.load(open(os.path.join(GOLD, name)))
+    say("plan mincopy golden", name)
+    _, out = gpu_plan(m, g["topk_idx"], g["E"], g["B"], planner="mincopy")
+    assert npi(out["cu"]).tolist() == g["cu_seqlens"]
+    assert npi(out["dest"]).tolist() == g["dest_idx"]
+    assert npi(out["stats"]).tolist() == g["stats"]
+    assert npi(out["slots"]).tolist() == g["slot_expert"]
+
+
+def test_plan_mincopy_example3_counts(m):
+    g = json.load(open(os.path.join(GOLD, "plan_example3_counts.json")))
+    lst = np.repeat(np.arange(g["E"]), g["expert_counts"])  # token t takes the ids at t and t + R*S
+    T = g["R"] * g["S"]
+    topk = np.stack([lst[k * T:(k + 1) * T] for k in range(g["K"])], axis=1).reshape(g["R"], g["S"], g["K"])
+    say("plan mincopy example 3")
+    _, out = gpu_plan(m, topk, g["E"], g["B"], planner="mincopy")
+    assert npi(out["stats"]).tolist() == g["mincopy"]["stats"]
+    assert npi(out["slots"])[3].tolist() == g["mincopy"]["slot_expert_rank3"]
+    assert_plan_equal(out, oplanner.plan(topk, g["E"], g["B"], planner="mincopy"), g["B"])
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_plan_mincopy_random_bit_exact(m, seed):
+    topk, E, B = small_plan_case(seed)
+    say("plan mincopy random", seed, topk.shape, E, B)
+    _, out = gpu_plan(m, topk, E, B, planner="mincopy")
+    p = oplanner.plan(topk, E, B, planner="mincopy")
+    assert_plan_equal(out, p, B)
+    if topk.size <= 4000:
+        check_plan_invariants(topk, E, B, npi(out["cu"]), npi(out["slots"]) if B else np.zeros((topk.shape[0], 0)),
+                              npi(out["dest"]), npi(out["src"]), npi(out["stats"]), planner="mincopy")
+
+
+@pytest.mark.parametrize("R,E,B,S,K", [
+    (4, 16, 4, 64, 2), (3, 12, 0, 777, 3), (1, 5, 2, 1000, 5), (8, 64, 8, 2731, 6), (16, 64, 1, 300, 4),
+    (2048, 4096, 2, 2, 2), (512, 4096, 8, 8, 4), (2048, 2048, 3, 3, 5), (2, 4096, 4, 3, 1500),
+    (2, 512, 8, 500, 16),    # 256 experts per rank: the keep count of each walks its rank's 256 counts
+])
+def test_plan_mincopy_shapes_bit_exact(m, R, E, B, S, K):
+    rng = np.random.default_rng(R * 1000 + S + 1)
+    topk = random_routing(rng, R, S, K, E, 2.5)
+    say("plan mincopy shape", R, E, B, S, K)
+    _, out = gpu_plan(m, topk, E, B, planner="mincopy")
+    assert_plan_equal(out, oplanner.plan(topk, E, B, planner="mincopy"), B)
 
 
 def test_plan_empty_routing(m):
