@@ -140,6 +140,23 @@ int moonep_plan_ex(moonep_dims d, int32_t planner, const int32_t* topk_idx, int3
                    int32_t* src_of_row, int32_t* stats, void* workspace, moonep_stream stream);
 
 /*
+ * moonep_plan_static -- moonep_plan_ex for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  It takes no workspace: the
+ * planner's scratch is a device array inside the library, moonep_plan_static_scratch_bytes() (8 MiB)
+ * large, of which every GPU the library runs on holds its own copy until the process ends.  The call
+ * allocates and frees nothing.  Arguments, outputs and limits are those of moonep_plan_ex; dims whose
+ * moonep_plan_workspace_bytes exceed the scratch size are refused with MOONEP_EINVAL (use moonep_plan_ex
+ * with a workspace then).  Every call on one GPU uses that GPU's one array: calls that overlap on a GPU
+ * (concurrent streams, or threads) race and give unspecified plans; calls in stream order do not.  No
+ * scratch contents carry over between calls (every planner kernel writes its part before reading it).
+ * MOONEP_EHIP when the array's device address cannot be obtained on the current device.
+ */
+size_t moonep_plan_static_scratch_bytes(void);
+int moonep_plan_static(moonep_dims d, int32_t planner, const int32_t* topk_idx, int32_t* expert_counts,
+                       double* maxvio, int32_t* cu_seqlens, int32_t* slot_expert, int32_t* dest_idx,
+                       int32_t* src_of_row, int32_t* stats, moonep_stream stream);
+
+/*
  * moonep_dispatch -- fused permute ([P2] "Core technique": each token row is
  * written straight into its expert-grouped row of the fixed S*K buffer).
  *   Xp[dest_idx[r,s,k], :] = X[r,s,:] for every k; rows with dest -1 are skipped.

@@ -15,7 +15,7 @@ from ._lib import (  # noqa: F401
     Dims, MoonepError, LIB_PATH, SYMBOLS, MOONEP_F32, MOONEP_BF16, MOONEP_PLAN_PREFIX, MOONEP_PLAN_MINCOPY,
     PLANNERS, make_dims, last_error,
     moonep_plan_workspace_bytes, moonep_group_gemm_workspace_bytes, moonep_wgrad_workspace_bytes, moonep_plan,
-    moonep_plan_ex,
+    moonep_plan_ex, moonep_plan_static, moonep_plan_static_scratch_bytes,
     moonep_dispatch, moonep_prefetch, moonep_group_gemm, moonep_combine, moonep_wgrad, moonep_reduce_grad,
     moonep_combine_backward, moonep_group_gemm_dgrad, moonep_dispatch_backward, moonep_swiglu,
     moonep_swiglu_backward,

@@ -60,6 +60,8 @@ def _load():
         "moonep_plan_workspace_bytes": (sz, [Dims]),
         "moonep_plan": (ctypes.c_int, [Dims, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
         "moonep_plan_ex": (ctypes.c_int, [Dims, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
+        "moonep_plan_static_scratch_bytes": (sz, []),
+        "moonep_plan_static": (ctypes.c_int, [Dims, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
         "moonep_dispatch": (ctypes.c_int, [Dims, i32, ctypes.c_int, vp, vp, vp, vp]),
         "moonep_prefetch": (ctypes.c_int, [Dims, i32, i32, ctypes.c_int, vp, vp, vp, vp]),
         "moonep_group_gemm_workspace_bytes": (sz, [Dims]),
@@ -84,8 +86,8 @@ def _load():
 _LIB = _load()
 
 # exported symbol names, as declared in include/moonep.h
-SYMBOLS = ("moonep_last_error", "moonep_plan_workspace_bytes", "moonep_plan", "moonep_plan_ex", "moonep_dispatch",
-           "moonep_prefetch",
+SYMBOLS = ("moonep_last_error", "moonep_plan_workspace_bytes", "moonep_plan", "moonep_plan_ex",
+           "moonep_plan_static_scratch_bytes", "moonep_plan_static", "moonep_dispatch", "moonep_prefetch",
            "moonep_group_gemm_workspace_bytes", "moonep_group_gemm", "moonep_combine",
            "moonep_wgrad_workspace_bytes", "moonep_wgrad", "moonep_reduce_grad", "moonep_combine_backward",
            "moonep_group_gemm_dgrad", "moonep_dispatch_backward", "moonep_swiglu", "moonep_swiglu_backward")
@@ -191,6 +193,24 @@ def moonep_plan_ex(d: Dims, planner, topk_idx, expert_counts, maxvio, cu_seqlens
     if workspace.numel() * workspace.element_size() < moonep_plan_workspace_bytes(d):
         raise ValueError("plan workspace too small")
     _check(_LIB.moonep_plan_ex(d, _planner_code(planner), *args, _stream(stream)))
+
+
+def moonep_plan_static_scratch_bytes() -> int:
+    return int(_LIB.moonep_plan_static_scratch_bytes())
+
+
+def moonep_plan_static(d: Dims, planner, topk_idx, expert_counts, maxvio, cu_seqlens, slot_expert, dest_idx,
+                       src_of_row, stats, stream=None):
+    """moonep_plan_ex without a workspace: the library's own per-GPU scratch array serves instead (calls that
+    overlap on one GPU race on it)."""
+    import torch
+    i32 = torch.int32
+    _check(_LIB.moonep_plan_static(
+        d, _planner_code(planner), _ptr(topk_idx, "topk_idx", i32, d.N),
+        _ptr(expert_counts, "expert_counts", i32, d.E), _ptr(maxvio, "maxvio", torch.float64, 1),
+        _ptr(cu_seqlens, "cu_seqlens", i32, d.R * (d.E + d.B + 1)),
+        _ptr(slot_expert, "slot_expert", i32, d.R * d.B, optional=d.B == 0), _ptr(dest_idx, "dest_idx", i32, d.N),
+        _ptr(src_of_row, "src_of_row", i32, d.N, optional=True), _ptr(stats, "stats", i32, 4), _stream(stream)))
 
 
 def moonep_dispatch(d: Dims, H: int, X, dest_idx, Xp, stream=None):

@@ -27,6 +27,7 @@
 //               ballot match + per-wave LDS counters, tiles processed in order),
 //               then its destination row.
 #include <algorithm>
+#include <mutex>
 
 #include "block_scan.h"
 #include "moonep_common.h"
@@ -537,3 +538,64 @@ extern "C" int moonep_plan_ex(moonep_dims d, int32_t planner, const int32_t* top
   return MOONEP_OK;
 }
 
+// ------------------------------------------------------------------ allocation-free planning
+
+namespace {
+
+// Scratch of moonep_plan_static: the planner's workspace in a device array the library owns.  Every GPU
+// the library runs on holds its own copy (a __device__ variable exists once per device) until the
+// process ends.  Host code never passes `scratch` itself to a kernel -- in host code the name is a
+// host-side stand-in -- but the device address hipGetSymbolAddress returns for the current device.
+constexpr size_t kStaticScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array, looked up once per device (with that device
+// current); nullptr and a message on failure.
+void* static_scratch() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    moonep::set_error("moonep_plan_static: no usable current device (%s)", hipGetErrorString(e));
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      moonep::set_error("moonep_plan_static: hipGetSymbolAddress of the scratch array failed on device %d: %s", dev,
+                        hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" size_t moonep_plan_static_scratch_bytes(void) { return kStaticScratchBytes; }
+
+extern "C" int moonep_plan_static(moonep_dims d, int32_t planner, const int32_t* topk_idx, int32_t* expert_counts,
+                                  double* maxvio, int32_t* cu_seqlens, int32_t* slot_expert, int32_t* dest_idx,
+                                  int32_t* src_of_row, int32_t* stats, moonep_stream stream) {
+  if (int rc = check_dims(d, "moonep_plan_static")) return rc;
+  const size_t need = plan_ws(d, nullptr).bytes;
+  MOONEP_REQUIRE(need <= kStaticScratchBytes,
+                 "moonep_plan_static: these dims need %zu bytes of planner scratch, more than the %zu bytes the "
+                 "library holds per GPU; use moonep_plan_ex with a workspace",
+                 need, kStaticScratchBytes);
+  // the pointer checks of moonep_plan_ex come first, so a bad call touches no device state
+  MOONEP_REQUIRE(expert_counts && maxvio && cu_seqlens && stats, "moonep_plan_static: null output pointer");
+  MOONEP_REQUIRE(d.B == 0 || slot_expert, "moonep_plan_static: slot_expert is null with B > 0");
+  MOONEP_REQUIRE(n_pairs(d) == 0 || (topk_idx && dest_idx), "moonep_plan_static: null topk_idx or dest_idx");
+  void* ws = static_scratch();
+  if (ws == nullptr) return MOONEP_EHIP;
+  // every planner kernel writes its part of the workspace before reading it: nothing needs clearing
+  return moonep_plan_ex(d, planner, topk_idx, expert_counts, maxvio, cu_seqlens, slot_expert, dest_idx, src_of_row,
+                        stats, ws, stream);
+}

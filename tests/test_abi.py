@@ -55,6 +55,7 @@ def test_bad_dims_rejected_everywhere(dims, msg):
     calls = [
         lambda: L.moonep_plan(d, *([null] * 10)),
         lambda: L.moonep_plan_ex(d, 1, *([null] * 10)),
+        lambda: L.moonep_plan_static(d, 0, *([null] * 9)),
         lambda: L.moonep_dispatch(d, 8, 1, null, null, null, null),
         lambda: L.moonep_prefetch(d, 8, 8, 1, null, null, null, null),
         lambda: L.moonep_group_gemm(d, 8, 8, 1, *([null] * 7)),
@@ -95,6 +96,18 @@ def test_plan_ex_rejects_an_unknown_planner():
     assert "null" in m.last_error()  # a valid planner gets as far as the pointer checks
     with pytest.raises(ValueError, match="planner"):
         _lib._planner_code("optimal")
+
+
+def test_static_plan_refuses_sizes_beyond_its_scratch():
+    # refused on the host, before the scratch array's device address is looked up
+    d = m.make_dims(64, 4096, 4, 65536, 8)  # 4 Mi pairs over 4096 experts: 128 MiB of block histograms
+    L = _lib.lib()
+    assert m.moonep_plan_workspace_bytes(d) > L.moonep_plan_static_scratch_bytes() == 8 << 20
+    assert L.moonep_plan_static(d, 0, *([None] * 8), None) == _lib.MOONEP_EINVAL
+    assert "scratch" in m.last_error()
+    small = m.make_dims(2, 4, 1, 3, 1)
+    assert L.moonep_plan_static(small, 0, *([None] * 8), None) == _lib.MOONEP_EINVAL
+    assert "null" in m.last_error()
 
 
 def test_null_pointers_rejected():
