@@ -169,6 +169,21 @@ def test_plan_mincopy_shapes_bit_exact(m, R, E, B, S, K):
     assert_plan_equal(out, oplanner.plan(topk, E, B, planner="mincopy"), B)
 
 
+def test_plan_mincopy_counts_invalid_and_repeated_ids(m):
+    rng = np.random.default_rng(4)
+    topk = random_routing(rng, 2, 50, 3, 8, 1.5)
+    topk[0, 3, 1] = 8       # out of range
+    topk[1, 7, 0] = -2      # negative
+    topk[1, 9, 2] = topk[1, 9, 0]  # repeated within a token
+    say("plan mincopy invalid ids")
+    _, out = gpu_plan(m, topk, 8, 2, planner="mincopy")
+    assert npi(out["stats"])[3] == 3
+    dest = npi(out["dest"])
+    assert dest[0, 3, 1] == -1 and dest[1, 7, 0] == -1
+    valid = dest[dest >= 0]
+    assert len(np.unique(valid)) == len(valid) and valid.max() < topk.size
+
+
 def test_plan_empty_routing(m):
     say("plan empty")
     topk = np.zeros((4, 0, 2), dtype=np.int64)

@@ -63,3 +63,40 @@ def test_static_plan_equals_plan_with_workspace(m, planner):
             assert torch.equal(got[k], ref[k]), (name, k)
         assert npi(got["cu"])[:, -1].tolist() == [wl.P] * wl.R
 
+
+
+def test_static_plan_in_a_captured_graph(m):
+    # the use it is for: captured once (after one eager call has looked up the scratch address), replayed
+    # with new routings written into the same input buffer, each replay equal to an eager moonep_plan_ex
+    from load_balanced_dispatch_amd import _lib
+    lib = _lib.lib()
+    wl = WORKLOADS["mid_fwd"]
+    d = m.make_dims(wl.R, wl.E, wl.B, wl.S, wl.K)
+    topk = torch.zeros((wl.R, wl.S, wl.K), dtype=torch.int32, device=DEV)
+    got = outputs(wl, -9)
+    routings = [router_output(wl.R, wl.S, wl.E, wl.K, 0, alpha=alpha_for(wl, 0, t))[0] for t in (0.0, 1.0, 3.0)]
+    topk.copy_(torch.as_tensor(routings[0]))
+    say("static plan graph: eager warm-up")
+    assert call(lib, "moonep_plan_static", d, 1, topk, got) == 0, m.last_error()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            assert call(lib, "moonep_plan_static", d, 1, topk, got) == 0, m.last_error()
+    torch.cuda.current_stream().wait_stream(s)
+    ws = torch.empty(m.moonep_plan_workspace_bytes(d), dtype=torch.uint8, device=DEV)
+    for rep, idx in enumerate(routings + routings[:1]):
+        say("static plan graph: replay", rep)
+        topk.copy_(torch.as_tensor(idx))
+        for t in got.values():
+            t.fill_(-5)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = outputs(wl, -7)
+        assert call(lib, "moonep_plan_ex", d, 1, topk, ref, ws) == 0
+        torch.cuda.synchronize()
+        for k in ref:
+            assert torch.equal(got[k], ref[k]), (rep, k)
