@@ -19,8 +19,18 @@ from ._lib import Dims, make_dims
 
 
 class MoeLayer:
+    """One balanced MoE projection layer.
+
+    `slot_pool` = (W_slots [R,B,H,Hp] of the layer dtype, dW_slots [R,B,H,Hp] float32 or None) makes the
+    layer use a caller's slot buffers instead of its own: the pages keep one process-wide pool of B
+    slots that every layer shares, so the extra memory is B experts in total, not B per layer.  Layers
+    sharing a pool run one after another; a layer's backward that follows other layers' forward passes
+    re-runs its prefetch first (the pool then holds the other layers' slots), and its reduce_grad leaves
+    the slot gradients at zero for the next layer.
+    """
+
     def __init__(self, R, E, B, S, K, H, Hp=None, dtype=torch.bfloat16, device="cuda", backward=False,
-                 src_of_row=True, data_grad=False, planner="prefix"):
+                 src_of_row=True, data_grad=False, planner="prefix", slot_pool=None):
         self.d: Dims = make_dims(R, E, B, S, K)
         self.planner = planner  # "prefix" (home-first) or "mincopy" (fewest copies)
         d = self.d
@@ -42,9 +52,15 @@ class MoeLayer:
         # activations
         self.X = torch.zeros((R, S, H), dtype=dtype, device=device)
         self.Xp = torch.empty((N, H), dtype=dtype, device=device)
+        pool_w, pool_dw = slot_pool if slot_pool is not None else (None, None)
         if Hp is not None:
             self.W_home = torch.zeros((E, H, Hp), dtype=dtype, device=device)
-            self.W_slots = torch.zeros((R, B, H, Hp), dtype=dtype, device=device)
+            if pool_w is not None:
+                if tuple(pool_w.shape) != (R, B, H, Hp) or pool_w.dtype != dtype:
+                    raise ValueError(f"slot pool must be [{R},{B},{H},{Hp}] {dtype}")
+                self.W_slots = pool_w
+            else:
+                self.W_slots = torch.zeros((R, B, H, Hp), dtype=dtype, device=device)
             self.Yp = torch.empty((N, Hp), dtype=dtype, device=device)
             self.ws_gemm = torch.empty(max(1, _lib.moonep_group_gemm_workspace_bytes(d)), dtype=torch.uint8,
                                        device=device)
@@ -52,7 +68,12 @@ class MoeLayer:
             if backward:
                 self.dY = torch.zeros((N, Hp), dtype=dtype, device=device)
                 self.dW_home = torch.zeros((E, H, Hp), dtype=torch.float32, device=device)
-                self.dW_slots = torch.zeros((R, B, H, Hp), dtype=torch.float32, device=device)
+                if pool_dw is not None:
+                    if tuple(pool_dw.shape) != (R, B, H, Hp) or pool_dw.dtype != torch.float32:
+                        raise ValueError(f"slot gradient pool must be [{R},{B},{H},{Hp}] float32")
+                    self.dW_slots = pool_dw
+                else:
+                    self.dW_slots = torch.zeros((R, B, H, Hp), dtype=torch.float32, device=device)
                 self.ws_wgrad = torch.empty(max(1, _lib.moonep_wgrad_workspace_bytes(d)), dtype=torch.uint8,
                                             device=device)
                 if data_grad:
