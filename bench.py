@@ -682,6 +682,33 @@ def runtime_copy_gbs(reps=5):
     return 2 * (1 << 30) / (ms * 1e-3) / 1e9
 
 
+def library_copy_gbs(reps=5):
+    """HBM rate of this library's own copy kernel, the prefetch, used as a plain copy: eight [8192, 8192]
+    bf16 experts (1 GiB) into the eight slots of one rank, timed with events after one untimed pass; the
+    2 GiB moved per pass is far larger than the last-level cache.  The ceiling the prefetch stage could
+    reach in isolation, beside its rate inside the step."""
+    import torch
+
+    import load_balanced_dispatch_amd as m
+    E, H = 8, 8192
+    d = m.make_dims(1, E, E, 1, 1)
+    W = torch.ones((E, H, H), dtype=torch.bfloat16, device="cuda")
+    Ws = torch.empty((1, E, H, H), dtype=torch.bfloat16, device="cuda")
+    slots = torch.arange(E, dtype=torch.int32, device="cuda").reshape(1, E)
+    m.moonep_prefetch(d, H, H, W, slots, Ws)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        m.moonep_prefetch(d, H, H, W, slots, Ws)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del W, Ws
+    torch.cuda.empty_cache()
+    return 2 * E * H * H * 2 / (ms * 1e-3) / 1e9
+
+
 def vendor_gemm_tflops(wl, reps=5):
     """The vendor BLAS (hipBLASLt via torch.matmul, bf16) on the group GEMM's FLOPs: R dense GEMMs of
     [P, H] x [H, H'] (forward shape) and of [H, P] x [P, H'] (the weight-gradient shape), all
@@ -1033,8 +1060,9 @@ def main():
         log("timing the CPU oracle's plan + dispatch on a bounded sample")
         cpu = cpu_baseline(wl, args.seed, h["alpha"])
 
-    log("timing the runtime's 1 GiB device copy (reference rate)")
+    log("timing the runtime's 1 GiB device copy and the library's copy kernel (reference rates)")
     copy_gbs = runtime_copy_gbs()
+    lib_copy_gbs = library_copy_gbs()
     if vendor:
         for n, key in (("group_gemm", "fwd"), ("dgrad", "fwd"), ("wgrad", "wgrad")):
             for entry in [rooflines.get(n), (next_rows or {}).get(n)] + ([roofline] if roofline.get("stage") == n else []):
@@ -1063,11 +1091,13 @@ def main():
         "rooflines": rooflines,
         "next_rows": next_rows,
         "cpu_baseline": cpu,
-        "reference_rates": {"runtime_copy_GBs": round(copy_gbs, 1),
+        "reference_rates": {"runtime_copy_GBs": round(copy_gbs, 1), "library_copy_GBs": round(lib_copy_gbs, 1),
                             "vendor_gemm_fwd_TFLOPs": round(vendor["fwd"], 1) if vendor else None,
                             "vendor_gemm_wgrad_TFLOPs": round(vendor["wgrad"], 1) if vendor else None,
                             "note": "the HIP runtime's device copy of 1 GiB (read + write), HIP events; a GB/s "
-                                    "stage's frac_of_runtime_copy is its rate over this. vendor_gemm_*: "
+                                    "stage's frac_of_runtime_copy is its rate over this. library_copy: this "
+                                    "library's prefetch kernel copying 1 GiB (eight [8192, 8192] bf16 experts) "
+                                    "outside the step. vendor_gemm_*: "
                                     "hipBLASLt (torch.matmul, bf16) on the same FLOPs as R dense GEMMs, "
                                     "[P,H]x[H,H'] and [H,P]x[P,H']; a GEMM stage's frac_of_vendor_gemm is its "
                                     "flop rate over that."},
