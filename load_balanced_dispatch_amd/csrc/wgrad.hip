@@ -148,6 +148,53 @@ __global__ __launch_bounds__(1024) void wgrad_schedule(const int32_t* __restrict
 
 namespace wg {
 constexpr int BH = 256, BN = 256, BK = 32, STAGES = 4, NWAVES = 8;
+constexpr int kMaxRanks = 4096;             // the MFMA kernel's limit on R (one bit per rank in LDS)
+constexpr int kMaskWords = kMaxRanks / 64;
+constexpr int kLdsRanks = 512;              // ranks whose segment bounds are also kept in LDS
+
+// Walks the row segments of one job like SegWalk, but from a per-unit table in LDS: a bit per rank
+// whose segment of this job is non-empty, and the bounds of the first kLdsRanks ranks' segments.
+// Inside the chunk loop a compiler-visible global load would make the compiler wait for every
+// load the wave has in flight, the DMA of the next chunks included (it cannot count the DMA
+// issued from asm); the table keeps the walk off global memory there for R <= kLdsRanks.
+struct LdsWalk {
+  const int32_t* cu;
+  const uint64_t* mask;
+  const int32_t *lo, *hi;
+  int G1, P, col;
+  int r, r_end;  // current rank, one past the last rank
+  int m, end;    // current row and end of the current segment (global rows)
+
+  __device__ bool seek(int from) {
+    from = __builtin_amdgcn_readfirstlane(from);  // uniform, so the walk branches on scalars
+    const int nwords = (r_end + 63) >> 6;
+    for (int wi = from >> 6; wi < nwords; ++wi) {
+      uint64_t bits = mask[wi];
+      bits = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(bits >> 32)) << 32) |
+             (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)bits);
+      if (wi == (from >> 6)) bits &= ~uint64_t(0) << (from & 63);
+      if (bits) {
+        r = __builtin_amdgcn_readfirstlane((wi << 6) + __builtin_ctzll(bits));
+        if (r >= r_end) break;
+        if (r < kLdsRanks) {
+          m = __builtin_amdgcn_readfirstlane(lo[r]);
+          end = __builtin_amdgcn_readfirstlane(hi[r]);
+        } else {
+          m = r * P + cu[(int64_t)r * G1 + col];
+          end = r * P + cu[(int64_t)r * G1 + col + 1];
+        }
+        return true;
+      }
+    }
+    r = r_end;
+    return false;
+  }
+  __device__ bool next(int step) {
+    m += step;
+    if (m < end) return true;
+    return seek(r + 1);
+  }
+};
 constexpr int X_STAGE = BK * BH;  // 32 token rows x 256 h; 64-byte blocks XOR-swizzled by row
 constexpr int D_STAGE = BK * BN;  // 32 token rows x 256 n; same layout
 constexpr int STAGE = X_STAGE + D_STAGE;
@@ -185,6 +232,8 @@ __global__ __launch_bounds__(512, 1) void wgrad_bf16(const uint16_t* __restrict_
                                                      int E, int B, int P, int H, int Hp) {
   __shared__ __attribute__((aligned(1024))) uint16_t lds[LDS_ELEMS];
   __shared__ int32_t s_unit[2];
+  __shared__ uint64_t s_mask[kMaskWords];           // this unit's job: ranks with a non-empty segment
+  __shared__ int32_t s_lo[kLdsRanks], s_hi[kLdsRanks];  // their global row bounds (ranks < kLdsRanks)
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int wm = w >> 2, wn = w & 3;
   const int HT = (H + BH - 1) / BH, NT = (Hp + BN - 1) / BN;  // H % 128 == 0, H' % 64 == 0
@@ -217,10 +266,27 @@ __global__ __launch_bounds__(512, 1) void wgrad_bf16(const uint16_t* __restrict_
     }
     __syncthreads();
     const int pos = s_unit[0], tile = s_unit[1];
-    __syncthreads();  // every wave holds the unit before thread 0 may claim the next one
-    if (pos < 0) break;
-    const int job = sorted_job[pos];
-    const int nchunks = sorted_chunks[pos];
+    if (pos < 0) break;  // uniform: every thread read the same s_unit
+    const int job = __builtin_amdgcn_readfirstlane(sorted_job[pos]);
+    const int nchunks = __builtin_amdgcn_readfirstlane(sorted_chunks[pos]);
+    const int col = job < E ? job : E + (job - E) % B;
+    const int only = job < E ? -1 : (job - E) / B;  // a slot job reads one rank's group
+    for (int r0 = 0; r0 < R; r0 += 512) {
+      const int r = r0 + t;
+      int a = 0, b = 0;
+      if (r < R && (only < 0 || r == only)) {
+        a = cu[(int64_t)r * (E + B + 1) + col];
+        b = cu[(int64_t)r * (E + B + 1) + col + 1];
+      }
+      const uint64_t bits = __ballot(b > a);
+      if (lane == 0 && (r0 >> 6) + w < ((R + 63) >> 6)) s_mask[(r0 >> 6) + w] = bits;
+      if (r < kLdsRanks) {
+        s_lo[r] = r * P + a;
+        s_hi[r] = r * P + b;
+      }
+    }
+    __syncthreads();  // the walk table is complete, and every wave holds the unit before thread 0 may
+                      // claim the next one
     const int h0 = (tile / NT) * BH, n0 = (tile % NT) * BN;
     const int width = min(BN, Hp - n0);
     // a partial tile (H % 256 or H' % 256 != 0) leaves whole 128-row or 64-column wave strips idle;
@@ -238,8 +304,17 @@ __global__ __launch_bounds__(512, 1) void wgrad_bf16(const uint16_t* __restrict_
       x_col[i] = (q * 4 + (s_l & 3)) * 8;
       d_col[i] = x_col[i];
     }
-    SegWalk walk = make_walk(cu, job, R, E, B, P);
-    walk.seek(walk.r);
+    LdsWalk walk;
+    walk.cu = cu;
+    walk.mask = s_mask;
+    walk.lo = s_lo;
+    walk.hi = s_hi;
+    walk.G1 = E + B + 1;
+    walk.P = P;
+    walk.col = col;
+    walk.r_end = only < 0 ? R : only + 1;
+    walk.m = walk.end = 0;
+    walk.seek(only < 0 ? 0 : only);
     int issued = 0;
     auto issue_next = [&]() {  // DMA of chunk `issued` into its ring slot, then advance the walker
       const uint32_t st = lds0 + (uint32_t)((issued % STAGES) * STAGE * 2 + wu * 2 * 1024);  // + (2w + i) KB
@@ -454,8 +529,8 @@ extern "C" int moonep_wgrad(moonep_dims d, int32_t H, int32_t Hp, moonep_dtype t
   const int64_t jobs = (int64_t)d.E + (int64_t)d.R * d.B;
   MOONEP_REQUIRE(jobs < (int64_t(1) << 28), "moonep_wgrad: too many jobs");
   const int P = d.S * d.K;
-  const bool mfma = t == MOONEP_BF16 && H % 128 == 0 && Hp % 64 == 0 && aligned16(Xp) && aligned16(dY) &&
-                    aligned16(dW_home) && (d.B == 0 || aligned16(dW_slots));
+  const bool mfma = t == MOONEP_BF16 && H % 128 == 0 && Hp % 64 == 0 && d.R <= wg::kMaxRanks && aligned16(Xp) &&
+                    aligned16(dY) && aligned16(dW_home) && (d.B == 0 || aligned16(dW_slots));
   if (mfma) {
     const int cus = device_cu_count();
     const int64_t units = jobs * ((H + wg::BH - 1) / wg::BH) * ((Hp + wg::BN - 1) / wg::BN);

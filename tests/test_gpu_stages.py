@@ -363,6 +363,8 @@ def test_combine_dispatch_round_trip(m):
     (torch.bfloat16, 2, 4, 2, 300, 2, 256, 256),    # MFMA path, several 64-row chunks, ragged segments
     (torch.bfloat16, 4, 8, 1, 100, 3, 512, 128),    # MFMA path with direct reads (B=1)
     (torch.bfloat16, 3, 6, 0, 90, 2, 256, 384),     # MFMA path, no slots
+    (torch.bfloat16, 72, 72, 1, 24, 4, 128, 64),    # MFMA path, home jobs read on ranks of two 64-rank words
+    (torch.bfloat16, 520, 520, 0, 8, 2, 128, 64),   # MFMA path, ranks past the 512 whose bounds sit in LDS
     (torch.bfloat16, 2, 4, 1, 40, 2, 40, 72),       # generic bf16
     (torch.float32, 4, 16, 4, 64, 2, 128, 256),     # float32
 ])
