@@ -709,6 +709,55 @@ def library_copy_gbs(reps=5):
     return 2 * E * H * H * 2 / (ms * 1e-3) / 1e9
 
 
+def _evict(buf):
+    """Writes a 1 GiB buffer, twice the size of the last-level cache, so that what follows starts cold."""
+    buf.fill_(7)
+
+
+def cold_copy_gbs(total_bytes, reps=5):
+    """The HIP runtime's device copy moving `total_bytes` (half read, half written), each pass timed alone
+    with events after the caches are evicted: the same-size cold reference of a bandwidth stage."""
+    import torch
+    half = max(256, (int(total_bytes) // 2 + 255) // 256 * 256)
+    src = torch.ones(half, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    ev = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst.copy_(src)
+    ms = 0.0
+    for _ in range(reps):
+        _evict(ev)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        ms += a.elapsed_time(b) / reps
+    del src, dst, ev
+    torch.cuda.empty_cache()
+    return 2 * half / (ms * 1e-3) / 1e9
+
+
+def cold_prefetch_gbs(L, nbytes, reps=5):
+    """The prefetch stage on the current plan with cold weights: each call timed alone with events after
+    the caches are evicted (inside the step the weights it reads may still sit in the last-level cache)."""
+    import torch
+    ev = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    L.plan()
+    L.prefetch()
+    ms = 0.0
+    for _ in range(reps):
+        _evict(ev)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        L.prefetch()
+        b.record()
+        torch.cuda.synchronize()
+        ms += a.elapsed_time(b) / reps
+    del ev
+    torch.cuda.empty_cache()
+    return nbytes / (ms * 1e-3) / 1e9
+
+
 def vendor_gemm_tflops(wl, reps=5):
     """The vendor BLAS (hipBLASLt via torch.matmul, bf16) on the group GEMM's FLOPs: R dense GEMMs of
     [P, H] x [H, H'] (forward shape) and of [H, P] x [P, H'] (the weight-gradient shape), all
@@ -1039,6 +1088,19 @@ def main():
         sweep_mincopy = {"sweep": sw_mc, "sweep_flatness": flat_mc}
         L.planner = "prefix"
     vendor = vendor_gemm_tflops(wl) if (wl.Hp is not None and wl.dtype == "bf16") else None
+    cold = None
+    if not args.no_extras:
+        log("cold-cache references: the prefetch with evicted caches, and same-size cold copies")
+        load_inputs(L, wl, args.seed, h["alpha"])
+        cold = {"prefetch_cold_GBs": (round(cold_prefetch_gbs(L, alg["prefetch"]), 1) if alg.get("prefetch")
+                                      else None)}
+        for n, entry in rooflines.items():
+            if n in ("prefetch", "dispatch", "combine", "reduce_grad") and "tflops" not in entry and alg.get(n):
+                ref = cold_copy_gbs(alg[n])
+                cold[f"{n}_same_bytes_cold_copy_GBs"] = round(ref, 1)
+                entry["frac_of_cold_copy_same_bytes"] = round(entry["achieved"] / ref, 4)
+                if roofline.get("stage") == n:
+                    roofline["frac_of_cold_copy_same_bytes"] = entry["frac_of_cold_copy_same_bytes"]
     del L
     torch.cuda.empty_cache()
 
@@ -1094,10 +1156,15 @@ def main():
         "reference_rates": {"runtime_copy_GBs": round(copy_gbs, 1), "library_copy_GBs": round(lib_copy_gbs, 1),
                             "vendor_gemm_fwd_TFLOPs": round(vendor["fwd"], 1) if vendor else None,
                             "vendor_gemm_wgrad_TFLOPs": round(vendor["wgrad"], 1) if vendor else None,
+                            "cold": cold,
                             "note": "the HIP runtime's device copy of 1 GiB (read + write), HIP events; a GB/s "
                                     "stage's frac_of_runtime_copy is its rate over this. library_copy: this "
                                     "library's prefetch kernel copying 1 GiB (eight [8192, 8192] bf16 experts) "
-                                    "outside the step. vendor_gemm_*: "
+                                    "outside the step. cold: the headline prefetch timed alone after a 1 GiB "
+                                    "write evicts the caches, and for each GB/s stage the runtime's copy of "
+                                    "the stage's algorithmic bytes (half read, half written) timed the same "
+                                    "way; a stage's frac_of_cold_copy_same_bytes is its in-step rate over "
+                                    "that. vendor_gemm_*: "
                                     "hipBLASLt (torch.matmul, bf16) on the same FLOPs as R dense GEMMs, "
                                     "[P,H]x[H,H'] and [H,P]x[P,H']; a GEMM stage's frac_of_vendor_gemm is its "
                                     "flop rate over that."},
