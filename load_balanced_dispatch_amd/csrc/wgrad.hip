@@ -77,7 +77,10 @@ __device__ __forceinline__ SegWalk make_walk(const int32_t* cu, int job, int R, 
 //   [kSchedHdr + p]           job at position p of the size order (p < n)
 //   [kSchedHdr + J + p]       its number of 32-row chunks
 //   [kSchedHdr + 2J + job]    chunk count of every job (scratch)
+//   [zero_row_word(J) ...]    512 zero bytes (128 words, 256-byte aligned): the source of the rows
+//                             past a segment's end, which must add nothing
 constexpr int kQueues = 8, kSchedHdr = 32 * (1 + kQueues), kBuckets = 512;
+__host__ __device__ constexpr int64_t zero_row_word(int64_t J) { return (kSchedHdr + 3 * J + 63) / 64 * 64; }
 
 // 32-row chunks of a job: each contributing rank's segment rounded up, as the kernel walks them.
 __device__ __forceinline__ int job_chunks(const int32_t* cu, int job, int R, int E, int B) {
@@ -144,6 +147,7 @@ __global__ __launch_bounds__(1024) void wgrad_schedule(const int32_t* __restrict
   }
   if (t == 0) ws[0] = n;
   if (t < kQueues) ws[32 * (1 + t)] = 0;
+  if (t < 128) ws[zero_row_word(J) + t] = 0;
 }
 
 namespace wg {
@@ -205,9 +209,6 @@ static_assert(NWAVES * 32 * SP * 2 <= LDS_ELEMS, "epilogue staging must fit in t
 
 __device__ __forceinline__ int blk_off(int k, int n) { return k * 256 + ((((n >> 5) ^ (k & 3)) << 5) | (n & 31)); }
 
-// One 512-byte row of zeros: rows past a segment's end load from here, so they add nothing.
-__device__ __attribute__((aligned(16))) uint16_t zero_row[256];
-
 __device__ __forceinline__ bf16x8 operand_rows(const uint16_t* T, int k0, int c0, int lane) {
   const int grp = lane >> 4, c = lane & 15;
   const int col = c0 + 16 * (grp & 1) + 4 * (c & 3);
@@ -243,6 +244,10 @@ __global__ __launch_bounds__(512, 1) void wgrad_bf16(const uint16_t* __restrict_
   const int32_t* sorted_job = ws + kSchedHdr;
   const int32_t* sorted_chunks = sorted_job + J;
   const int home_q = blockIdx.x % kQueues;
+  // rows past a segment's end are loaded from the workspace's zero row (addressed from a kernel
+  // argument: a global symbol's address would be reloaded from memory at every DMA issue, and that
+  // scalar load's wait would also wait for the wave's LDS reads in flight)
+  const uint16_t* zero_row = reinterpret_cast<const uint16_t*>(ws + zero_row_word(J));
   const uint32_t lds0 = lds_addr(lds);                            // LDS byte address of the ring
   const int wu = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, uniform
   int qd = 0;  // thread 0: queues home_q .. home_q + qd - 1 (mod 8) are known to be empty
@@ -511,7 +516,7 @@ using namespace moonep;
 extern "C" size_t moonep_wgrad_workspace_bytes(moonep_dims d) {
   if (check_dims(d, "moonep_wgrad_workspace_bytes") != MOONEP_OK) return 0;
   const size_t jobs = (size_t)d.E + (size_t)d.R * d.B;
-  return (((size_t)kSchedHdr + 3 * jobs) * sizeof(int32_t) + 255) & ~size_t(255);
+  return (((size_t)zero_row_word((int64_t)jobs) + 128) * sizeof(int32_t) + 255) & ~size_t(255);
 }
 
 extern "C" int moonep_wgrad(moonep_dims d, int32_t H, int32_t Hp, moonep_dtype t, const void* Xp, const void* dY,
