@@ -22,7 +22,8 @@
 //   plan_solve  one 1024-thread block: keep counts (home-first prefix, or the
 //               fewest-copies choice of overflowing experts), overflow/deficit
 //               prefix sums, slot assignment, cu_seqlens, stats, maxvio.
-//               O(E + R + R*(E+B)), plus O(E*E/R) for the fewest-copies keep.
+//               O(E + R + R*(E+B)), plus O(E*E/R) for the fewest-copies keep;
+//               a handful of block-wide scans, each a few DPP steps per wave.
 //   plan_emit   grid = U: stable rank of every pair inside its expert (wave
 //               ballot match + per-wave LDS counters, tiles processed in order),
 //               then its destination row.
@@ -195,17 +196,19 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(
   int32_t* sefirst = sdefs + R; // [R]
   int32_t* sncopy = sefirst + R;// [R]
   int32_t* solist = sT;         // [E] the overflowing experts, ascending (sT is dead by then)
-  __shared__ int32_t wsum[kSolveThreads / 64];
+  __shared__ int32_t wsum[3 * (kSolveThreads / 64)];
   __shared__ int32_t red[3][kSolveThreads / 64];
   const int t = threadIdx.x, nt = blockDim.x, lane = t & 63, w = t >> 6, nw = nt >> 6;
   const int per = E / R;
 
-  int mx = 0, bad = 0;
-  for (int e = t; e < E; e += nt) {
+  // the first count and error word of each thread are loaded together, so that their round trips overlap
+  int mx = t < E ? counts[t] : 0, bad = t < U ? err[t] : 0;
+  if (t < E) sT[t] = mx;
+  for (int e = t + nt; e < E; e += nt) {
     sT[e] = counts[e];
     mx = max(mx, sT[e]);
   }
-  for (int u = t; u < U; u += nt) bad += err[u];
+  for (int u = t + nt; u < U; u += nt) bad += err[u];
   mx = wave_max(mx);
   bad = wave_sum(bad);
   if (lane == 0) {
@@ -223,27 +226,30 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(
     stats[3] = b;
   }
 
+  // exclusive prefix of T over all experts (a rank's home experts are contiguous), in sovs for now:
+  // the pairs routed to rank r's experts before e are pre[e] - pre[r * per], its load
+  // pre[(r + 1) * per] - pre[r * per] (the total for the last rank)
+  for (int e = t; e < E; e += nt) sovs[e] = sT[e];
+  __syncthreads();
+  int tot3[3];
+  block_excl_scan3(sovs, E, nullptr, 0, nullptr, 0, wsum, tot3);
+  const int32_t* pre = sovs;
+  const int totT = tot3[0];
+  auto rank_load = [&](int r) { return (r + 1 < R ? pre[(r + 1) * per] : totT) - pre[r * per]; };
   if (planner == MOONEP_PLAN_PREFIX) {
     // home-first keep counts: each rank keeps the first P pairs of its experts in ascending order
-    for (int r = t; r < R; r += nt) {
-      int before = 0;
-      for (int e = r * per; e < (r + 1) * per; ++e) {
-        const int k = min(max(P - before, 0), sT[e]);
-        skeep[e] = k;
-        sover[e] = sT[e] - k;
-        before += sT[e];
-      }
-      sdef[r] = max(0, P - before);
+    for (int e = t; e < E; e += nt) {
+      const int before = pre[e] - pre[(e / per) * per];
+      const int k = min(max(P - before, 0), sT[e]);
+      skeep[e] = k;
+      sover[e] = sT[e] - k;
     }
+    for (int r = t; r < R; r += nt) sdef[r] = max(0, P - rank_load(r));
   } else {
     // fewest copies: an overloaded rank's excess x leaves through its experts taken largest first
     // (equal counts: lower id first).  Expert e overflows what x still needs after the experts ahead
     // of it in that order, clamped to [0, T_e]; one thread per expert, O(E/R) each.
-    for (int r = t; r < R; r += nt) {
-      int load = 0;
-      for (int e = r * per; e < (r + 1) * per; ++e) load += sT[e];
-      sdef[r] = P - load;  // signed for now: minus the excess of an overloaded rank
-    }
+    for (int r = t; r < R; r += nt) sdef[r] = P - rank_load(r);  // signed for now: minus the excess
     __syncthreads();
     for (int e = t; e < E; e += nt) {
       const int r = e / per, te = sT[e], x = -sdef[r];
@@ -269,9 +275,7 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(
   }
   for (int r = t; r < R; r += nt) sdefs[r] = sdef[r];
   __syncthreads();
-  block_excl_scan(sovs, E, wsum);
-  block_excl_scan(snpos, E, wsum);
-  block_excl_scan(sdefs, R, wsum);
+  block_excl_scan3(sovs, E, snpos, E, sdefs, R, wsum, tot3);
 
   // contiguous cut.  Deficit rank d's interval [lo, hi) of the overflow list overlaps the experts
   // e in [a, z) with over[e] > 0, where a is the first e with ovstart + over > lo and z the first
@@ -310,7 +314,7 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(
   const int G = E + B;
   for (int d = w; d < R; d += nw) {
     const int d0 = sdefs[d], d1 = d0 + sdef[d];
-    const int nf = snpos[sefirst[d]];
+    const int nf = snpos[sefirst[d]], ncp = sncopy[d];
     int carry = 0;
     if (lane == 0) cu[(int64_t)d * (G + 1)] = 0;
     for (int g0 = 0; g0 < G; g0 += 64) {
@@ -325,7 +329,7 @@ __global__ __launch_bounds__(kSolveThreads) void plan_solve(
         }
       } else if (g < G) {
         const int jj = g - E;  // slot jj < B of rank d, from the LDS tables (not the global output)
-        const int e = jj < sncopy[d] ? solist[snpos[sefirst[d]] + jj] : -1;
+        const int e = jj < ncp ? solist[nf + jj] : -1;
         if (e >= 0) c = overlap(sovs[e], sovs[e] + sover[e], d0, d1);
       }
       const int incl = wave_incl_scan(c);
