@@ -289,8 +289,8 @@ size_t moonep_wgrad_workspace_bytes(moonep_dims d);
  * In:  Xp [R*S*K,H], dY [R*S*K,Hp] dtype t;  cu_seqlens [R,E+B+1].
  * In/Out: dW_home [E,H,Hp] float32;  dW_slots [R,B,H,Hp] float32 (NULL when B == 0).
  * workspace: moonep_wgrad_workspace_bytes(d) bytes of device memory (256-byte aligned), contents
- * ignored on entry (it holds the size-ordered list of gradient jobs that have rows and the work
- * queue counters, which the call itself resets before use).
+ * ignored on entry (it holds the size-ordered list of gradient jobs that have rows, the work
+ * queue counters and a row of zeros, all of which the call itself writes before use).
  */
 int moonep_wgrad(moonep_dims d, int32_t H, int32_t Hp, moonep_dtype t, const void* Xp, const void* dY,
                  const int32_t* cu_seqlens, float* dW_home, float* dW_slots, void* workspace,
