@@ -880,6 +880,16 @@ def extra_workloads(args, alpha_of, no_ffn):
         "group_gemm_tflops": rl1["group_gemm"]["tflops"], "rooflines": rl1, "sweep": [x for x in sweep
                                                                                     if x["maxvio_target"] != 2.0],
         "sweep_flatness": sweep_summary(wl, L, res, [t for t in pts if t != 2.0])[1]}
+    if not args.no_extras:
+        # the mid prefetch moves few, small copies whose home weights may still be in the last-level cache
+        # in the step: each sweep point's prefetch alone with cold caches, beside its in-step rate
+        cold = {}
+        for tgt in [head] + [t for t in pts if t != head]:
+            nbytes = 2 * wl.H * wl.Hp * 2 * int(res[tgt]["stats"][1])
+            if nbytes:
+                load_inputs(L, wl, args.seed, res[tgt]["alpha"])
+                cold[str(tgt)] = round(cold_prefetch_gbs(L, nbytes), 1)
+        out["mid_fwd"]["prefetch_cold_GBs"] = cold
     wb = WORKLOADS["mid_bwd"]
     _, rl2 = point_rooflines(wb, L, res[2.0])
     out["mid_bwd"] = {"workload": wb.description, "maxvio_target": 2.0, "maxvio": round(res[2.0]["maxvio"], 4),
