@@ -16,8 +16,9 @@
 //     with ds_read_b128, the weight operand (k along LDS rows, as the [H, H'] layout stores it)
 //     with ds_read_b64_tr_b16; both LDS layouts are XOR-swizzled against bank conflicts.  The
 //     epilogue rounds one 32-row strip at a time to bf16 in LDS and writes whole 16-byte chunks.
-//   * ggemm_generic<T> is a plain LDS-tiled FMA kernel for float32 and for bf16 shapes the MFMA
-//     kernel does not tile (H % 32 or H' % 64 != 0).
+//   * ggemm_generic<T> is a plain LDS-tiled kernel for float32 and for bf16 shapes the bf16 MFMA
+//     kernel does not tile (H % 32 or H' % 64 != 0): 64 x 64 x 16 block tiles held as float32 in
+//     LDS, four waves of 32 x 32, each a chain of float32 MFMA 32x32x2 steps.
 #include "block_scan.h"
 #include "mfma_tile.h"
 #include "moonep_common.h"
@@ -322,6 +323,10 @@ __global__ __launch_bounds__(512, 1) void ggemm_bf16(const uint16_t* __restrict_
 }  // namespace fwd
 
 // ------------------------------------------------------------------ generic kernel
+//
+// One 256-thread block per 64 x 64 output tile (grid-stride over the 64-row tile prefix), K in steps
+// of 16 staged as float32 in LDS (bf16 widened exactly), zeros past a group's rows and past K;
+// four waves of 32 x 32 reduce with v_mfma_f32_32x32x2_f32.
 
 template <typename T>
 __device__ __forceinline__ float load_elem(const T* p);
@@ -344,7 +349,7 @@ __global__ __launch_bounds__(256) void ggemm_generic(const T* __restrict__ Xp, c
                                                      int E, int B, int P, int H, int Hp) {
   __shared__ float As[kGenBK][kGenBM + 4];
   __shared__ float Bs[kGenBK][kGenBN + 4];
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;  // 2 x 2 waves of 32 x 32
   const int K = BT ? Hp : H, N = BT ? H : Hp;  // reduction length and output width (as in ggemm_bf16)
   const int G = E + B, G1 = G + 1, NG = R * G;
   const int NT = (N + kGenBN - 1) / kGenBN;
@@ -359,7 +364,7 @@ __global__ __launch_bounds__(256) void ggemm_generic(const T* __restrict__ Xp, c
     const int64_t row0 = (int64_t)r * P + c0 + mo;
     const T* Wg = g < E ? W_home + (int64_t)g * H * Hp : W_slots + ((int64_t)r * B + (g - E)) * H * Hp;
     const int n0 = nt * kGenBN;
-    float acc[4][4] = {};
+    f32x16 acc = (f32x16)(0.f);
     for (int k0 = 0; k0 < K; k0 += kGenBK) {
       for (int i = threadIdx.x; i < kGenBK * kGenBM; i += 256) {
         const int m = i / kGenBK, k = i % kGenBK;
@@ -372,28 +377,15 @@ __global__ __launch_bounds__(256) void ggemm_generic(const T* __restrict__ Xp, c
       }
       __syncthreads();
 #pragma unroll
-      for (int k = 0; k < kGenBK; ++k) {
-        float a[4], b[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = As[k][ty * 4 + i];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) b[j] = Bs[k][tx * 4 + j];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
-      }
+      for (int k = 0; k < kGenBK; k += 2)
+        acc = mfma32_f32(As[k + (lane >> 5)][wm * 32 + (lane & 31)], Bs[k + (lane >> 5)][wn * 32 + (lane & 31)], acc);
       __syncthreads();
     }
+    const int n = n0 + wn * 32 + (lane & 31);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = ty * 4 + i;
-      if (m >= rows) continue;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int n = n0 + tx * 4 + j;
-        if (n < N) store_elem(Yp + (row0 + m) * N + n, acc[i][j]);
-      }
+    for (int v = 0; v < 16; ++v) {
+      const int m = wm * 32 + acc_row(v, lane);
+      if (m < rows && n < N) store_elem(Yp + (row0 + m) * N + n, acc[v]);
     }
   }
 }

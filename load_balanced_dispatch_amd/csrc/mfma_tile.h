@@ -27,6 +27,12 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// v_mfma_f32_32x32x2_f32: lane l supplies A[m = l%32][k = l/32] and B[k = l/32][n = l%32]; the
+// accumulator layout is that of the bf16 32x32 instruction (acc_row below).
+__device__ __forceinline__ f32x16 mfma32_f32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
 // 64 lanes x 16 bytes: lane l copies 16 bytes from its global address g to LDS byte address
 // lds_byte + 16*l (global_load_lds_dwordx4; lds_byte must be wave-uniform).  Issued from asm so
 // the compiler does not wait for every outstanding load before each LDS read: the kernels wait on

@@ -13,7 +13,10 @@
 // MFMA 32x32x16 bf16 by eight waves; both operands reduce along token rows, so
 // both are read from LDS with ds_read_b64_tr_b16.  A job without rows writes
 // nothing.  The float32 read-modify-write of dW goes through LDS so it moves
-// whole 16-byte row chunks.
+// whole 16-byte row chunks.  float32 inputs, and bf16 shapes that kernel does not
+// tile (H % 128 or H' % 64 != 0), take wgrad_generic: 64 x 64 output tiles per
+// block, 16-row chunks staged as float32 in LDS, four waves of 32 x 32 reducing
+// with v_mfma_f32_32x32x2_f32.
 #include "block_scan.h"
 #include "mfma_tile.h"
 #include "moonep_common.h"
@@ -461,14 +464,14 @@ __global__ __launch_bounds__(256) void wgrad_generic(const T* __restrict__ Xp, c
                                                      int Hp) {
   __shared__ float Xs[kGenBK][kGenBH + 4];
   __shared__ float Ds[kGenBK][kGenBN + 4];
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;  // 2 x 2 waves of 32 x 32
   const int HT = (H + kGenBH - 1) / kGenBH, NT = (Hp + kGenBN - 1) / kGenBN;
   const int job = blockIdx.x / (HT * NT), rem = blockIdx.x % (HT * NT);
   const int h0 = (rem / NT) * kGenBH, n0 = (rem % NT) * kGenBN;
   SegWalk walk = make_walk(cu, job, R, E, B, P);
   if (!walk.seek(walk.r)) return;
   float* out = job < E ? dW_home + (int64_t)job * H * Hp : dW_slots + (int64_t)(job - E) * H * Hp;
-  float acc[4][4] = {};
+  f32x16 acc = (f32x16)(0.f);
   do {
     for (int i = threadIdx.x; i < kGenBK * kGenBH; i += 256) {
       const int mr = i / kGenBH, h = i % kGenBH;
@@ -480,30 +483,17 @@ __global__ __launch_bounds__(256) void wgrad_generic(const T* __restrict__ Xp, c
     }
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < kGenBK; ++k) {
-      float a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = Xs[k][ty * 4 + i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = Ds[k][tx * 4 + j];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
-    }
+    for (int k = 0; k < kGenBK; k += 2)
+      acc = mfma32_f32(Xs[k + (lane >> 5)][wm * 32 + (lane & 31)], Ds[k + (lane >> 5)][wn * 32 + (lane & 31)], acc);
     __syncthreads();
   } while (walk.next(kGenBK));
+  const int n = n0 + wn * 32 + (lane & 31);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int h = h0 + ty * 4 + i;
-    if (h >= H) continue;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + tx * 4 + j;
-      if (n < Hp) {
-        float* p = out + (int64_t)h * Hp + n;
-        *p = *p + acc[i][j];
-      }
+  for (int v = 0; v < 16; ++v) {
+    const int h = h0 + wm * 32 + acc_row(v, lane);
+    if (h < H && n < Hp) {
+      float* p = out + (int64_t)h * Hp + n;
+      *p = *p + acc[v];
     }
   }
 }
