@@ -78,6 +78,12 @@ def parse():
     ap.add_argument("--mfma-md", metavar="COUNTER_CSV",
                     help="print the MFMA utilisation of the GEMM kernels from a --profile-pass counter run of "
                          + " ".join(MFMA_COUNTERS) + "; no GPU")
+    ap.add_argument("--vendor-pass", action="store_true",
+                    help="for counter runs: only the vendor BLAS GEMMs the GEMM stages are compared with (the "
+                         "forward shape, then the weight-gradient shape, each 2 + R calls); prints no JSON")
+    ap.add_argument("--vendor-mfma-md", metavar="COUNTER_CSV",
+                    help="print the MFMA utilisation of the vendor GEMM kernels of a --vendor-pass counter run of "
+                         + " ".join(MFMA_COUNTERS) + "; no GPU")
     ap.add_argument("--profile-pass", action="store_true",
                     help="for counter runs: 1 warm-up + --steps steps of the whole path, then one plain 1 GiB "
                          "device copy whose FETCH_SIZE/WRITE_SIZE calibrate the traffic counters; prints no JSON")
@@ -764,10 +770,10 @@ def vendor_gemm_tflops(wl, reps=5):
     operands contiguous 2-D tensors, timed with events.  Context for the MFMA fraction: the same work
     with one weight per P = S*K rows, an easier reuse pattern than the ragged groups."""
     import torch
-    P, H, Hp, R = wl.S * wl.K, wl.H, wl.Hp, wl.R
+    R = wl.R
     g = torch.Generator(device="cuda").manual_seed(1)
     out = {}
-    for name, (m, k, n) in (("fwd", (P, H, Hp)), ("wgrad", (H, P, Hp))):
+    for name, m, k, n in vendor_shapes(wl):
         a = torch.randn((m, k), device="cuda", dtype=torch.bfloat16, generator=g)
         b = torch.randn((k, n), device="cuda", dtype=torch.bfloat16, generator=g)
         for _ in range(2):
@@ -784,6 +790,61 @@ def vendor_gemm_tflops(wl, reps=5):
         del a, b
     torch.cuda.empty_cache()
     return out
+
+
+def vendor_shapes(wl):
+    """(name, m, k, n) of the dense GEMMs vendor_gemm_tflops times, in the order it runs them."""
+    P, H, Hp = wl.S * wl.K, wl.H, wl.Hp
+    return (("fwd", P, H, Hp), ("wgrad", H, P, Hp))
+
+
+def vendor_pass(wl):
+    """The vendor GEMMs of vendor_gemm_tflops, 2 + R calls of each shape in turn, for a counter run."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(1)
+    for _, m, k, n in vendor_shapes(wl):
+        a = torch.randn((m, k), device="cuda", dtype=torch.bfloat16, generator=g)
+        b = torch.randn((k, n), device="cuda", dtype=torch.bfloat16, generator=g)
+        for _ in range(2 + wl.R):
+            torch.matmul(a, b)
+        torch.cuda.synchronize()
+        del a, b
+    torch.cuda.empty_cache()
+
+
+def vendor_mfma_markdown(counter_csv, wl):
+    """MFMA utilisation of the vendor GEMM kernels of a --vendor-pass counter run, per call.
+
+    Every dispatch that issues MFMAs is a vendor GEMM call; the first 2 + R belong to the forward shape and
+    the next 2 + R to the weight-gradient shape (vendor_pass runs them in that order).  The instruction the
+    library picks need not be this path's 32x32x16, so the rate is taken from the busy cycles (1024 flop per
+    SIMD and busy cycle at the dense bf16 rate) and checked against 2*m*k*n per call."""
+    per = {}
+    for r in csv.DictReader(open(counter_csv)):
+        d = per.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"]})
+        d["dur_s"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+    calls = [per[i] for i in sorted(per) if per[i].get("SQ_VALU_MFMA_BUSY_CYCLES", 0) > 0
+             and all(c in per[i] for c in MFMA_COUNTERS)]
+    n_each = 2 + wl.R
+    lines = ["| shape (m x k x n) | call | kernel | us | engine clock GHz | MFMA busy / CU busy | TFLOP/s (busy cycles) "
+             "| TFLOP/s (2mkn) |", "|---|---|---|---|---|---|---|---|"]
+    rec = {"workload": wl.name, "counters": list(MFMA_COUNTERS), "shapes": {}}
+    for si, (name, m, k, n) in enumerate(vendor_shapes(wl)):
+        rows = calls[si * n_each:(si + 1) * n_each]
+        out = []
+        for ci, d in enumerate(rows):
+            busy = d["SQ_VALU_MFMA_BUSY_CYCLES"] / (SIMDS_PER_CU * d["SQ_BUSY_CU_CYCLES"])
+            clock = d["SQ_BUSY_CU_CYCLES"] / N_CU / d["dur_s"] / 1e9
+            tf_busy = d["SQ_VALU_MFMA_BUSY_CYCLES"] * 1024 / d["dur_s"] / 1e12
+            tf = 2.0 * m * k * n / d["dur_s"] / 1e12
+            kname = d["name"].split("(")[0][:48]
+            lines.append(f"| {name} {m}x{k}x{n} | {ci} | `{kname}` | {d['dur_s'] * 1e6:.1f} | {clock:.2f} | "
+                         f"{busy:.3f} | {tf_busy:.0f} | {tf:.0f} |")
+            out.append({"us": round(d["dur_s"] * 1e6, 1), "engine_clock_ghz": round(clock, 3),
+                        "mfma_busy_of_cu_busy": round(busy, 4), "tflops": round(tf, 1)})
+        rec["shapes"][name] = {"m": m, "k": k, "n": n, "calls": out}
+    return "\n".join(lines), rec
 
 
 def calibration_copy():
@@ -1009,6 +1070,14 @@ def main():
         print(json.dumps(rec, indent=1))
         print("```")
         return
+    if args.vendor_mfma_md:
+        table, rec = vendor_mfma_markdown(args.vendor_mfma_md, wl)
+        print(table)
+        print()
+        print("```json")
+        print(json.dumps(rec, indent=1))
+        print("```")
+        return
     if args.ffn_traffic_md or args.traffic_md:
         if args.ffn_traffic_md:
             table, rec = ffn_traffic_markdown(args.ffn_traffic_md[0], args.ffn_traffic_md[1], wl)
@@ -1046,6 +1115,12 @@ def main():
             log("profile pass done: FFN passes, then a 1 GiB copy")
         else:
             print(json.dumps({"ffn": time_ffn(wl, args.seed, alpha_of(wl, head_target), args.steps, args.warmup)}))
+        return
+    if args.vendor_pass:
+        if wl.Hp is None:
+            raise SystemExit("--vendor-pass needs a workload with H'")
+        vendor_pass(wl)
+        log("vendor pass done:", [s[0] for s in vendor_shapes(wl)])
         return
     log(f"workload {wl.description}; building buffers")
     L = make_layer(wl, backward)

@@ -193,6 +193,43 @@ def test_mfma_table_from_counters(tmp_path):
     assert "`ggemm_bf16<false>` | group_gemm | 2 |" in table
 
 
+def test_vendor_mfma_table_splits_the_calls_by_shape(tmp_path):
+    # a vendor pass on the mid workload: 2 + R calls of the forward shape, then of the weight-gradient shape,
+    # with a copy kernel between them that issues no MFMA; each call's matrix pipes are busy 60% of its CU
+    # cycles at 1.5 GHz
+    from synthetic import WORKLOADS
+    wl = WORKLOADS["mid_fwd"]
+    path = str(tmp_path / "vendor.csv")
+    fields = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    shapes = bench.vendor_shapes(wl)
+    calls = [(s, 1_000_000 + 1000 * i) for s in shapes for i in range(2 + wl.R)]
+    calls.insert(2 + wl.R, (None, 5000))
+    rows = []
+    for disp, (shape, dur_ns) in enumerate(calls):
+        cu = 256 * 1.5e9 * dur_ns * 1e-9
+        vals = {"SQ_INSTS_MFMA": 1e6 if shape else 0, "SQ_BUSY_CU_CYCLES": cu,
+                "SQ_VALU_MFMA_BUSY_CYCLES": 0.6 * 4 * cu if shape else 0}
+        name = "Cijk_Ailk_Bljk_BBS_MT256x256x64(args)" if shape else "copy_kernel(args)"
+        for c, v in vals.items():
+            rows.append({"Dispatch_Id": disp, "Kernel_Name": name, "Counter_Name": c, "Counter_Value": v,
+                         "Start_Timestamp": 10_000_000 * disp, "End_Timestamp": 10_000_000 * disp + dur_ns})
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=fields)
+        w.writeheader()
+        w.writerows(rows)
+    table, rec = bench.vendor_mfma_markdown(path, wl)
+    assert list(rec["shapes"]) == ["fwd", "wgrad"]
+    fwd, wg = rec["shapes"]["fwd"], rec["shapes"]["wgrad"]
+    assert (fwd["m"], fwd["k"], fwd["n"]) == (wl.S * wl.K, wl.H, wl.Hp)
+    assert (wg["m"], wg["k"], wg["n"]) == (wl.H, wl.S * wl.K, wl.Hp)
+    assert len(fwd["calls"]) == len(wg["calls"]) == 2 + wl.R
+    c0 = fwd["calls"][0]
+    assert c0["engine_clock_ghz"] == 1.5 and c0["mfma_busy_of_cu_busy"] == 0.6 and c0["us"] == 1000.0
+    assert c0["tflops"] == round(2.0 * wl.S * wl.K * wl.H * wl.Hp / 1e-3 / 1e12, 1)
+    assert wg["calls"][0]["us"] == 1000.0  # the copy kernel between the shapes was skipped
+    assert "| fwd " in table and "`Cijk_Ailk_Bljk_BBS_MT256x256x64`" in table
+
+
 def test_stage_roofline_fraction_and_algorithmic_bytes():
     # the per-point roofline fractions of the sweep: achieved = algorithmic work / time, frac = achieved / peak;
     # prefetch moves 2*H*H'*b per slotted copy, reduce_grad 4*H*H'*(2 per expert with copies + 2 per copy)
