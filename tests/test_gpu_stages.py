@@ -367,6 +367,7 @@ def test_combine_dispatch_round_trip(m):
     (torch.bfloat16, 520, 520, 0, 8, 2, 128, 64),   # MFMA path, ranks past the 512 whose bounds sit in LDS
     (torch.bfloat16, 2, 4, 1, 40, 2, 40, 72),       # generic bf16
     (torch.float32, 4, 16, 4, 64, 2, 128, 256),     # float32
+    (torch.float32, 2, 6, 1, 70, 3, 72, 100),       # float32, partial 64 x 64 tiles in both H and H'
 ])
 def test_wgrad_accumulates(m, dtype, R, E, B, S, K, H, Hp):
     rng = np.random.default_rng(S + H)
