@@ -16,6 +16,8 @@
 //     with ds_read_b128, the weight operand (k along LDS rows, as the [H, H'] layout stores it)
 //     with ds_read_b64_tr_b16; both LDS layouts are XOR-swizzled against bank conflicts.  The
 //     epilogue rounds one 32-row strip at a time to bf16 in LDS and writes whole 16-byte chunks.
+//     Where N is a multiple of 512, a group's last m-tile of at most 128 rows runs as 128 x 512
+//     tiles, so that fewer rows past the group end are computed.
 //   * ggemm_generic<T> is a plain LDS-tiled kernel for float32 and for bf16 shapes the bf16 MFMA
 //     kernel does not tile (H % 32 or H' % 64 != 0): 64 x 64 x 16 block tiles held as float32 in
 //     LDS, four waves of 32 x 32, each a chain of float32 MFMA 32x32x2 steps.
@@ -35,11 +37,21 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 int64_t n_groups(const moonep_dims& d) { return (int64_t)d.R * (d.E + d.B); }
 
-// workspace: tiles for BM = 256 then for BM = 64, each [NG + 1] ints
+// workspace: tiles of the bf16 kernel, then 64-row tiles of the generic kernel, each [NG + 1] ints
 size_t ggemm_ws_bytes(const moonep_dims& d) { return 2 * align256((size_t)(n_groups(d) + 1) * sizeof(int32_t)); }
 
-__global__ __launch_bounds__(1024) void ggemm_tiles(const int32_t* __restrict__ cu, int R, int E, int B,
-                                                   int32_t* __restrict__ t256, int32_t* __restrict__ t64) {
+// With tail tiles, a group of m rows runs as full-height (256-row) m-tiles times the 256-wide n-tiles,
+// except that a last m-tile of at most 128 rows runs as a 128-row m-tile times 512-wide n-tiles.
+__device__ __forceinline__ int full_mtiles(int m) {
+  const int rem = m & (kMfmaBM - 1);
+  return m / kMfmaBM + (rem > kMfmaBM / 2 ? 1 : 0);
+}
+
+// Per group, in t256: the bf16 kernel's tiles (with tail tiles: every tile of the group, N being a
+// multiple of 512; without: its 256-row m-tiles); in t64: the generic kernel's 64-row m-tiles.
+__global__ __launch_bounds__(1024) void ggemm_tiles(const int32_t* __restrict__ cu, int R, int E, int B, int N,
+                                                   int tails, int32_t* __restrict__ t256,
+                                                   int32_t* __restrict__ t64) {
   __shared__ int32_t wsum[16];
   const int G = E + B, NG = R * G;
   int carry256 = 0, carry64 = 0;
@@ -50,7 +62,12 @@ __global__ __launch_bounds__(1024) void ggemm_tiles(const int32_t* __restrict__ 
       const int r = i / G, g = i % G;
       m = cu[(int64_t)r * (G + 1) + g + 1] - cu[(int64_t)r * (G + 1) + g];
     }
-    const int a = (m + kMfmaBM - 1) / kMfmaBM, b = (m + kGenBM - 1) / kGenBM;
+    int a = (m + kMfmaBM - 1) / kMfmaBM;
+    if (tails) {
+      const int f = full_mtiles(m);
+      a = f * (N / kMfmaBM) + (m > f * kMfmaBM ? N / (2 * kMfmaBM) : 0);
+    }
+    const int b = (m + kGenBM - 1) / kGenBM;
     // two scans of this chunk
     const int ia = wave_incl_scan(a), ib = wave_incl_scan(b);
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
@@ -101,11 +118,17 @@ constexpr int OPS = 4;  // DMA instructions per wave per stage (2 for A, 2 for B
 constexpr int kBandM = 4;  // m-tiles per band of the tile raster
 constexpr int A_STAGE = BM * BK;  // 64-byte rows; 16-byte chunks XOR-swizzled by row
 constexpr int B_STAGE = BK * BN;  // 512-byte rows; 64-byte blocks XOR-swizzled by row
-constexpr int STAGE = A_STAGE + B_STAGE;
+constexpr int A_TAIL = BM / 2 * BK;  // a 128 x 512 tail tile's A stage
+// a ring slot holds a full tile's stage (A, then B) or, with tail tiles, a tail tile's (its 128-row
+// A, then B as two 256-column parts, each laid out like a full tile's B)
+template <bool TAILS>
+constexpr int STAGE = TAILS ? A_TAIL + 2 * B_STAGE : A_STAGE + B_STAGE;
 constexpr int WN = 64, TM = 4, TN = 2, KK = BK / 16;
 constexpr int SP = WN + 8;  // epilogue staging pitch (elements)
-constexpr int LDS_ELEMS = STAGES * STAGE;
-static_assert(NWAVES * 32 * SP <= LDS_ELEMS, "epilogue staging must fit in the ring");
+template <bool TAILS>
+constexpr int LDS_ELEMS = STAGES * STAGE<TAILS>;
+static_assert(NWAVES * 32 * SP <= LDS_ELEMS<false>, "epilogue staging must fit in the ring");
+static_assert(A_STAGE + B_STAGE <= STAGE<true> && LDS_ELEMS<true> * 2 <= 160 * 1024, "slot sizes");
 
 // A stage (rows = tokens, 4 chunks of 8 k-values per row): the chunk order is permuted per row so
 // that the 16-byte operand reads of 16 consecutive rows, and of the two k-halves of 8 rows, hit
@@ -131,69 +154,112 @@ __device__ __forceinline__ int b_off(int k, int n) { return k * BN + ((((n >> 5)
 // global_load_lds_dwordx4 into a 4-stage ring, three stages ahead of the MFMAs, with no
 // register staging.  The last n-tile may be narrower than 256 (H' % 256 != 0): its missing
 // columns load a repeated valid column and their waves skip MFMAs and stores.
-template <bool BT>
+//
+// TAILS (N a multiple of 512): a group whose last m-tile would hold at most 128 rows runs that tail
+// as 128 x 512 tiles (one row of eight 128 x 64 waves), which halves the rows computed past the group
+// end, and tiles are numbered group by group (each group's full m-tiles in bands, then its tail).
+template <bool BT, bool TAILS>
 __global__ __launch_bounds__(512, 1) void ggemm_bf16(const uint16_t* __restrict__ Xp,
                                                      const uint16_t* __restrict__ W_home,
                                                      const uint16_t* __restrict__ W_slots,
                                                      const int32_t* __restrict__ cu,
                                                      const int32_t* __restrict__ tstart, uint16_t* __restrict__ Yp,
                                                      int R, int E, int B, int P, int H, int Hp) {
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[LDS_ELEMS];
+  constexpr int kStage = STAGE<TAILS>;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[LDS_ELEMS<TAILS>];
   const int K = BT ? Hp : H, N = BT ? H : Hp;  // reduction length and output width
   const uint32_t lds0 = lds_addr(lds);                            // LDS byte address of the ring
   const int wu = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, uniform
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int wm = w >> 2, wn = w & 3;
+  const int wn = w & 3;  // the wave's 64-column strip inside a 256-column B part
   const int G = E + B, G1 = G + 1, NG = R * G;
   const int NT = (N + BN - 1) / BN;
-  const int total = tstart[NG] * NT;
+  const int total = TAILS ? tstart[NG] : tstart[NG] * NT;
   const int nblk = gridDim.x;
   const int vb = (nblk % 8 == 0) ? (int)(blockIdx.x % 8) * (nblk / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
   const int KT = K / BK;
   const int a_lr = lane >> 2, a_ls = lane & 3;   // A: one wave instruction fills 16 rows
   const int b_lr = lane >> 5, b_ls = lane & 31;  // B: one wave instruction fills 2 rows
 
-  const int MT = tstart[NG];
   for (int tile = vb; tile < total; tile += nblk) {
     // banded raster: bands of kBandM consecutive m-tiles, n-tile-major inside a band, so the 32
-    // tiles one XCD runs at once cover a kBandM x 8 block and reuse both operands in its L2
-    const int band = tile / (kBandM * NT), m0b = band * kBandM;
-    const int sb = min(kBandM, MT - m0b), rb = tile - band * kBandM * NT;
-    const int mt = m0b + rb % sb, nt = rb / sb;
-    const int grp = find_group(tstart, NG, mt);
+    // tiles one XCD runs at once cover a kBandM x 8 block and reuse both operands in its L2 (with
+    // tail tiles the bands are a group's own m-tiles, and its tail tiles follow them)
+    int grp, mt, nt;
+    bool tail = false;
+    if constexpr (TAILS) {
+      grp = find_group(tstart, NG, tile);
+      const int r_ = grp / G, g_ = grp % G;
+      const int mts = full_mtiles(cu[(int64_t)r_ * G1 + g_ + 1] - cu[(int64_t)r_ * G1 + g_]);
+      const int local = tile - tstart[grp];
+      if (local < mts * NT) {
+        const int band = local / (kBandM * NT), m0b = band * kBandM;
+        const int sb = min(kBandM, mts - m0b), rb = local - band * kBandM * NT;
+        mt = m0b + rb % sb;
+        nt = rb / sb;
+      } else {
+        mt = mts;
+        nt = local - mts * NT;
+        tail = true;
+      }
+    } else {
+      const int MT = tstart[NG];
+      const int band = tile / (kBandM * NT), m0b = band * kBandM;
+      const int sb = min(kBandM, MT - m0b), rb = tile - band * kBandM * NT;
+      const int mtg = m0b + rb % sb;
+      nt = rb / sb;
+      grp = find_group(tstart, NG, mtg);
+      mt = mtg - tstart[grp];
+    }
     const int r = grp / G, g = grp % G;
     const int c0 = cu[(int64_t)r * G1 + g], c1 = cu[(int64_t)r * G1 + g + 1];
-    const int mo = (mt - tstart[grp]) * BM;
-    const int rows = min(BM, c1 - c0 - mo);
+    const int mo = mt * BM;
+    const int rows = min(tail ? BM / 2 : BM, c1 - c0 - mo);
     const int64_t row0 = (int64_t)r * P + c0 + mo;
     const uint16_t* Wg = g < E ? W_home + (int64_t)g * H * Hp : W_slots + ((int64_t)r * B + (g - E)) * H * Hp;
-    const int n0 = nt * BN;
-    const int width = min(BN, N - n0);
-    const int strips = min(TM, max(0, (rows - wm * 128 + 31) / 32));  // valid 32-row strips of this wave
-    const bool wave_cols = wn * WN < width;
+    const int n0 = nt * (tail ? 2 * BN : BN);
+    const int width = min(tail ? 2 * BN : BN, N - n0);
+    // wave tile origin: 2 x 4 waves of 128 x 64 in a full tile, 1 x 8 in a tail tile, whose waves 4-7
+    // read the second B part
+    const int wr0 = tail ? 0 : (w >> 2) * 128, wc0 = tail ? w * WN : wn * WN;
+    const int b_at = tail ? A_TAIL + (w >> 2) * B_STAGE : A_STAGE;  // this wave's B part, elements into a slot
+    const int strips = min(TM, max(0, (rows - wr0 + 31) / 32));  // valid 32-row strips of this wave
+    const bool wave_cols = wc0 < width;
 
-    // global sources of this wave's four DMA instructions per stage (2 for A, 2 for B)
+    // global sources of this wave's DMA instructions per stage: 2 for A and 2 for B in a full tile,
+    // 1 for A and 2 for each B part in a tail tile
     const uint16_t* a_src[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int row = (2 * w + i) * 16 + a_lr;  // rows past the group end repeat its last row
+      const int row = tail ? w * 16 + a_lr : (2 * w + i) * 16 + a_lr;  // rows past the group end repeat its last row
       a_src[i] = Xp + (row0 + min(row, rows - 1)) * K + 8 * (a_ls ^ a_swz(row));
     }
-    const uint16_t* b_src[2];
+    const uint16_t* b_src[TAILS ? 4 : 2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < (TAILS ? 4 : 2); ++i) {
+      const int nb = n0 + (i >> 1) * BN;  // first column of B part i / 2
       if (BT) {  // output columns past N repeat the last one
-        const int row = (2 * w + i) * 16 + a_lr;
-        b_src[i] = Wg + (int64_t)min(n0 + row, N - 1) * Hp + 8 * (a_ls ^ a_swz(row));
+        const int row = (2 * w + (i & 1)) * 16 + a_lr;
+        b_src[i] = Wg + (int64_t)min(nb + row, N - 1) * Hp + 8 * (a_ls ^ a_swz(row));
       } else {
-        const int k = (2 * w + i) * 2 + b_lr;
+        const int k = (2 * w + (i & 1)) * 2 + b_lr;
         const int q = (b_ls >> 2) ^ (k & 3);
-        b_src[i] = Wg + (int64_t)k * Hp + min(n0 + (q * 4 + (b_ls & 3)) * 8, Hp - 8);
+        b_src[i] = Wg + (int64_t)k * Hp + min(nb + (q * 4 + (b_ls & 3)) * 8, Hp - 8);
       }
     }
     const int64_t b_step = BT ? BK : (int64_t)BK * Hp;  // one stage along k
-    auto issue = [&](int kt) {  // this wave's 1 KB pieces of stage kt: slot byte base + (2w + i) KB
-      const uint32_t st = lds0 + (uint32_t)((kt % STAGES) * STAGE * 2 + wu * 2 * 1024);
+    auto issue = [&](int kt) {  // this wave's 1 KB pieces of stage kt
+      const uint32_t sl = lds0 + (uint32_t)((kt % STAGES) * kStage * 2);
+      if constexpr (TAILS) {
+        if (tail) {
+          dma16(a_src[0] + kt * BK, sl + wu * 1024);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            dma16(b_src[i] + kt * b_step, sl + (A_TAIL + (i >> 1) * B_STAGE) * 2 + wu * 2 * 1024 + (i & 1) * 1024);
+          return;
+        }
+      }
+      const uint32_t st = sl + wu * 2 * 1024;  // slot byte base + (2w + i) KB
 #pragma unroll
       for (int i = 0; i < 2; ++i) dma16(a_src[i] + kt * BK, st + i * 1024);
 #pragma unroll
@@ -208,8 +274,8 @@ __global__ __launch_bounds__(512, 1) void ggemm_bf16(const uint16_t* __restrict_
 
     for (int st = 0; st < STAGES - 1 && st < KT; ++st) issue(st);
     auto frag = [&](int kt, int kk, bf16x8 (&a)[TM], bf16x8 (&b)[TN]) {
-      const uint16_t* As = lds + (kt % STAGES) * STAGE;
-      const uint16_t* Bs = As + A_STAGE;
+      const uint16_t* As = lds + (kt % STAGES) * kStage;
+      const uint16_t* Bs = As + b_at;
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         if (BT) {
@@ -226,7 +292,7 @@ __global__ __launch_bounds__(512, 1) void ggemm_bf16(const uint16_t* __restrict_
       }
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        const int row = wm * 128 + i * 32 + (lane & 31);
+        const int row = wr0 + i * 32 + (lane & 31);
         a[i] = *reinterpret_cast<const bf16x8*>(As + a_off(row, kk * 2 + (lane >> 5)));
       }
     };
@@ -264,11 +330,17 @@ __global__ __launch_bounds__(512, 1) void ggemm_bf16(const uint16_t* __restrict_
     };
     // barrier opening phase 2t: this wave has issued the stages up to min(t + 2, KT - 1), so
     // waiting until only the later ones are in flight means its share of stage t has landed, and
-    // the barrier extends that to every wave's share
+    // the barrier extends that to every wave's share (a tail tile's stage is 5 DMAs per wave)
     auto even_barrier = [&](int t) {
-      if (t + 2 < KT) wait_vmcnt<2 * OPS>();
-      else if (t + 1 < KT) wait_vmcnt<OPS>();
-      else wait_vmcnt<0>();
+      if (t + 2 < KT) {
+        if (tail) wait_vmcnt<2 * (OPS + 1)>();
+        else wait_vmcnt<2 * OPS>();
+      } else if (t + 1 < KT) {
+        if (tail) wait_vmcnt<OPS + 1>();
+        else wait_vmcnt<OPS>();
+      } else {
+        wait_vmcnt<0>();
+      }
       lds_barrier();
     };
     if (w < 4) {
@@ -310,9 +382,9 @@ __global__ __launch_bounds__(512, 1) void ggemm_bf16(const uint16_t* __restrict_
 #pragma unroll
         for (int q = lane; q < 32 * CPR; q += 64) {
           const int rr = q / CPR, cc = q % CPR;
-          const int row = wm * 128 + i * 32 + rr;
+          const int row = wr0 + i * 32 + rr;
           if (row < rows)
-            *reinterpret_cast<u32x4*>(Yp + (row0 + row) * N + n0 + wn * WN + cc * 8) =
+            *reinterpret_cast<u32x4*>(Yp + (row0 + row) * N + n0 + wc0 + cc * 8) =
                 *reinterpret_cast<const u32x4*>(stage + rr * SP + cc * 8);
         }
       }
@@ -430,15 +502,22 @@ int group_gemm_launch(const char* name, moonep_dims d, int32_t H, int32_t Hp, mo
   int32_t* t256 = static_cast<int32_t*>(workspace);
   int32_t* t64 = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
                                             align256((size_t)(n_groups(d) + 1) * sizeof(int32_t)));
-  hipLaunchKernelGGL(ggemm_tiles, dim3(1), dim3(1024), 0, s, cu_seqlens, d.R, d.E, d.B, t256, t64);
-  MOONEP_LAUNCH_CHECK(name);
   const int cus = device_cu_count();
   const int K = BT ? Hp : H, N = BT ? H : Hp;
   const bool mfma = t == MOONEP_BF16 && K % 32 == 0 && N % 64 == 0 && aligned16(A) && aligned16(W_home) &&
                     (d.B == 0 || aligned16(W_slots));
+  // tail tiles only where every 512-wide tail n-tile is whole (measured: on the 1408-wide output
+  // the kernel built with them ran 2-3% slower, tail tiles or not)
+  const bool tails = mfma && N % 512 == 0;
+  hipLaunchKernelGGL(ggemm_tiles, dim3(1), dim3(1024), 0, s, cu_seqlens, d.R, d.E, d.B, N, tails ? 1 : 0, t256, t64);
+  MOONEP_LAUNCH_CHECK(name);
   const int P = d.S * d.K;
-  if (mfma) {
-    hipLaunchKernelGGL(fwd::ggemm_bf16<BT>, dim3(cus), dim3(512), 0, s, static_cast<const uint16_t*>(A),
+  if (tails) {
+    hipLaunchKernelGGL((fwd::ggemm_bf16<BT, true>), dim3(cus), dim3(512), 0, s, static_cast<const uint16_t*>(A),
+                       static_cast<const uint16_t*>(W_home), static_cast<const uint16_t*>(W_slots), cu_seqlens, t256,
+                       static_cast<uint16_t*>(C), d.R, d.E, d.B, P, H, Hp);
+  } else if (mfma) {
+    hipLaunchKernelGGL((fwd::ggemm_bf16<BT, false>), dim3(cus), dim3(512), 0, s, static_cast<const uint16_t*>(A),
                        static_cast<const uint16_t*>(W_home), static_cast<const uint16_t*>(W_slots), cu_seqlens, t256,
                        static_cast<uint16_t*>(C), d.R, d.E, d.B, P, H, Hp);
   } else if (t == MOONEP_BF16) {
