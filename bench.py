@@ -303,12 +303,12 @@ STAGE_KERNELS = {
     "plan": r"^plan_(count|scan|solve|emit)$",
     "dispatch": r"^dispatch_rows<",
     "prefetch": r"^prefetch_slots<",
-    "group_gemm": r"^(ggemm_tiles$|ggemm_bf16<false>|ggemm_generic<.*false>)",
+    "group_gemm": r"^(ggemm_tiles$|ggemm_bf16<false\b|ggemm_generic<.*false>)",
     "combine": r"^combine_(vec|scalar)<[^>]*\btrue\b",
     "wgrad": r"^wgrad_(schedule|bf16|generic)",
     "reduce_grad": r"^reduce_grad_(kernel|scalar)",
     "combine_backward": r"^combine_bwd_",
-    "dgrad": r"^(ggemm_bf16<true>|ggemm_generic<.*true>)",
+    "dgrad": r"^(ggemm_bf16<true\b|ggemm_generic<.*true>)",
     "dispatch_backward": r"^combine_(vec|scalar)<[^>]*\bfalse\b",
     "swiglu": r"^swiglu_(vec|scalar)<",
     "swiglu_backward": r"^swiglu_bwd_",

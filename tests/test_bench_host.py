@@ -23,6 +23,8 @@ NAMES = {
     "tiles": "moonep::(anonymous namespace)::ggemm_tiles(moonep_dims, int const*, int*)",
     "fwd": "void moonep::fwd::(anonymous namespace)::ggemm_bf16<false>(moonep::fwd::GemmArgs)",
     "dgrad": "void moonep::fwd::(anonymous namespace)::ggemm_bf16<true>(moonep::fwd::GemmArgs)",
+    "fwd_tails": "void moonep::(anonymous namespace)::fwd::ggemm_bf16<false, true>(unsigned short const*, int, int)",
+    "dgrad_full": "void moonep::(anonymous namespace)::fwd::ggemm_bf16<true, false>(unsigned short const*, int, int)",
     "swiglu": "void moonep::(anonymous namespace)::swiglu_vec<unsigned short>(unsigned short const*, long, int)",
     "swiglu_bwd": "void moonep::(anonymous namespace)::swiglu_bwd_vec<unsigned short>(unsigned short const*)",
     "combine": "void moonep::(anonymous namespace)::combine_vec<8, 2, true, unsigned int, 6>(long)",
@@ -47,6 +49,7 @@ def test_more_than_one_gpu_is_refused():
 
 @pytest.mark.parametrize("key,base,stage", [
     ("fwd", "ggemm_bf16<false>", "group_gemm"), ("dgrad", "ggemm_bf16<true>", "dgrad"),
+    ("fwd_tails", "ggemm_bf16<false, true>", "group_gemm"), ("dgrad_full", "ggemm_bf16<true, false>", "dgrad"),
     ("tiles", "ggemm_tiles", "group_gemm"), ("combine", "combine_vec<8, 2, true, unsigned int, 6>", "combine"),
     ("dispatch_bwd", "combine_vec<8, 2, false, unsigned int, 6>", "dispatch_backward"), ("wgrad", "wgrad_bf16", "wgrad"),
     ("dispatch", "dispatch_rows<unsigned int __vector(4), false>", "dispatch"), ("swiglu_bwd",
