@@ -80,6 +80,8 @@ def test_combine_backward(m, dtype, D):
     (torch.bfloat16, 4, 16, 4, 160, 3, 128, 128),   # MFMA path, many small groups and slots, 128-wide n tile
     (torch.bfloat16, 3, 6, 0, 200, 2, 384, 64),     # MFMA path, no slots, direct reads, 2 n tiles
     (torch.bfloat16, 2, 4, 2, 200, 2, 64, 128),     # MFMA path, one 64-wide n tile (narrow wave layout)
+    (torch.bfloat16, 2, 4, 2, 300, 2, 512, 160),    # MFMA path with 128 x 512 tail tiles (N = H a multiple of 512)
+    (torch.bfloat16, 3, 6, 1, 170, 3, 1024, 96),    # tail tiles, two 512-wide tail n tiles, direct reads
     (torch.bfloat16, 2, 4, 1, 50, 2, 72, 40),       # generic bf16 path (H % 64 != 0)
     (torch.float32, 4, 16, 4, 64, 2, 128, 256),     # tiny workload shape, float32
     (torch.float32, 2, 6, 1, 37, 3, 33, 65),        # float32, ragged everything

@@ -289,6 +289,8 @@ def test_prefetch_several_items_per_block(m):
     (torch.bfloat16, 4, 16, 4, 160, 3, 128, 128),   # MFMA path, many small groups and slots
     (torch.bfloat16, 3, 6, 0, 200, 2, 64, 384),     # MFMA path, no slots, direct reads
     (torch.bfloat16, 2, 4, 2, 200, 2, 128, 320),    # MFMA path, 64-wide last n tile (narrow wave layout)
+    (torch.bfloat16, 2, 4, 2, 300, 2, 160, 512),    # MFMA path with 128 x 512 tail tiles (N a multiple of 512)
+    (torch.bfloat16, 3, 6, 1, 170, 3, 96, 1024),    # tail tiles, two 512-wide tail n tiles, direct reads
     (torch.bfloat16, 2, 4, 1, 50, 2, 40, 72),       # generic bf16 path (H % 64 != 0)
     (torch.float32, 4, 16, 4, 64, 2, 128, 256),     # tiny workload shape, float32
     (torch.float32, 2, 6, 1, 37, 3, 33, 65),        # float32, ragged everything
