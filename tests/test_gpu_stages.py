@@ -316,6 +316,40 @@ def test_group_gemm(m, dtype, R, E, B, S, K, H, Hp):
     assert_gemm_close(np64(Yp), ref, rel, "group_gemm")
 
 
+@pytest.mark.parametrize("dgrad", [False, True])
+def test_group_gemm_tail_tile_boundaries(m, dgrad):
+    """Groups whose last 256-row m-tile holds exactly 1, 127, 128 (a 128 x 512 tail tile) or 129 and 256
+    (a full tile) rows, with and without full m-tiles before them, on an output width that is a multiple
+    of 512 (tail tiles on) and on one that is not (off); cu_seqlens are set by hand, every row checked."""
+    R, E, B, K = 2, 8, 2, 1
+    sizes = [[128, 129, 1, 384, 385, 0, 256, 127, 0, 2],   # rank 0: home groups 0..7, then 2 slot groups
+             [512 + 128, 0, 200, 1, 0, 257, 128, 0, 5, 130]]  # rank 1
+    P = max(sum(r) for r in sizes)
+    for r, pad in ((0, 5), (1, 1)):  # fill each rank to P rows in one of its empty groups
+        sizes[r][pad] += P - sum(sizes[r])
+    cu = np.zeros((R, E + B + 1), dtype=np.int64)
+    for r in range(R):
+        cu[r, 1:] = np.cumsum(sizes[r])
+    assert (cu[:, -1] == P).all()
+    S = P // K
+    d = m.make_dims(R, E, B, S, K)
+    for K_, N_ in ((96, 512), (64, 1024), (96, 768)):
+        H, Hp = (N_, K_) if dgrad else (K_, N_)
+        A = rand_tensor((R * P, K_), torch.bfloat16, seed=N_ + K_)
+        W = rand_tensor((E, H, Hp), torch.bfloat16, seed=N_ + 1, std=H ** -0.5)
+        Ws = rand_tensor((R, B, H, Hp), torch.bfloat16, seed=N_ + 2, std=H ** -0.5)
+        C = torch.full((R * P, N_), float("nan"), dtype=torch.bfloat16, device=DEV)
+        ws = torch.empty(m.moonep_group_gemm_workspace_bytes(d), dtype=torch.uint8, device=DEV)
+        say("group_gemm tail boundaries", "dgrad" if dgrad else "fwd", H, Hp)
+        f = m.moonep_group_gemm_dgrad if dgrad else m.moonep_group_gemm
+        f(d, H, Hp, A, W, Ws, i32(cu), C, ws)
+        torch.cuda.synchronize()
+        A64, W64, Ws64 = (np.asarray(t.cpu().float().numpy(), dtype=np.float64) for t in (A, W, Ws))
+        g = olayer.group_gemm_dgrad if dgrad else olayer.group_gemm
+        ref = g(A64, W64, Ws64, cu, P)
+        assert_gemm_close(np64(C), ref, 1e-2, f"tail boundaries {'dgrad' if dgrad else 'fwd'} N={N_}")
+
+
 # ------------------------------------------------------------------ combine
 
 
